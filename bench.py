@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the normal-form batched adapter layer on one MI355X.
+
+A step is one forward of the whole layer (rotation, shrink, base GEMM with
+the s / b epilogue, expand, shared VeRA term) over one batch. The default
+workload is the mixed five-method decode batch: 4096 -> 4096, 128 tokens
+over 40 adapters (8 each of LoRA r16, DoRA r16, (IA)^3, VeRA with a shared
+rank-256 pair, OFT block 32), tokens assigned uniformly at random.
+
+Inputs are resident in HBM when timing starts. The timed loop cycles over
+several complete copies of the workload (x, W, y, every adapter, the VeRA
+pair) whose total exceeds twice the 256 MB Infinity Cache, so each forward
+streams its bytes from HBM rather than from the cache.
+
+Prints ONE JSON line. Also reports the roofline of the dominant kernel
+(algorithmic bytes per launch / its mean launch time from HIP events), the
+CPU oracle timed on the host, and the mixed-method overhead against the
+all-LoRA workload (4096 -> 4096, 128 tokens over 64 LoRA r16 adapters).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("mixed-adapter layer tokens/s + achieved HBM GB/s (% peak), 4096², 128 tok")
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, help="named workload index (0..4)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overhead", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def rotating_copies(wl, n_sets):
+    from lora_normal_form_amd import workload as glue
+    sets = []
+    for i in range(n_sets):
+        sets.append(glue.load(wl, device=0))
+    return sets
+
+
+def footprint_bytes(ld, wl, cost):
+    # bytes one copy of the workload occupies (x, W, y, adapters, VeRA pair)
+    return cost["bytes"] + (wl.vera_rank * (wl.d_in + wl.d_out) * 2 if wl.A_sh is not None else 0)
+
+
+def time_forwards(torch, sets, steps, warmup, profile=False):
+    from lora_normal_form_amd import scute
+    if profile:
+        for s in sets:
+            scute.scute_profile_enable(s.layer.h, True)
+            scute.scute_profile_read(s.layer.h)
+    for i in range(warmup):
+        s = sets[i % len(sets)]
+        s.layer.forward(s.batch, s.x, s.W, s.y)
+    torch.cuda.synchronize()
+    if profile:
+        for s in sets:
+            scute.scute_profile_read(s.layer.h)
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(steps):
+        s = sets[i % len(sets)]
+        s.layer.forward(s.batch, s.x, s.W, s.y)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    kernels = {}
+    if profile:
+        for s in sets:
+            for name, v in scute.scute_profile_read(s.layer.h).items():
+                k = kernels.setdefault(name, {"launches": 0, "total_ms": 0.0})
+                k["launches"] += v["launches"]
+                k["total_ms"] += v["total_ms"]
+            scute.scute_profile_enable(s.layer.h, False)
+    return gpu_ms, wall, kernels
+
+
+def dominant_kernel_bytes(name, wl, cost):
+    """Algorithmic bytes one launch of kernel ``name`` must move."""
+    es = 2 if wl.dtype == "bf16" else 4
+    xwy = wl.n * wl.d_in * es + wl.d_in * wl.d_out * es + wl.n * wl.d_out * 4
+    if name in ("forward", "fused"):
+        return cost["bytes"]
+    if name == "gemm":
+        return xwy
+    return None
+
+
+def cpu_baseline(wl, seconds):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.forward(wl)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": wl.n * reps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"whole batch ({wl.n} tokens) of the same workload, {reps} repetition(s), "
+                      f"{dt:.1f} s of numpy fp64 on {cores} BLAS thread(s)"}
+
+
+def measure(torch, wl, steps, warmup):
+    from lora_normal_form_amd import scute
+    first = rotating_copies(wl, 1)
+    cost = first[0].layer.cost(first[0].batch)
+    fp = footprint_bytes(first[0], wl, cost)
+    n_sets = max(2, int(math.ceil(2.2 * MALL_BYTES / fp)))
+    sets = first + rotating_copies(wl, n_sets - 1)
+    gpu_ms, wall, _ = time_forwards(torch, sets, steps, warmup)
+    _, _, kernels = time_forwards(torch, sets, steps, warmup, profile=True)
+    return {"cost": cost, "n_sets": n_sets, "gpu_ms": gpu_ms, "wall": wall, "kernels": kernels,
+            "sets": sets}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        sys.stderr.write("bench.py: this build measures one GPU only; --gpus must be 1 "
+                         "(the layer is token-parallel and shards with no in-layer "
+                         "communication, but nothing here runs on a second GPU)\n")
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py: no GPU visible\n")
+        sys.exit(1)
+    from synth import make_config
+    from lora_normal_form_amd import scute  # noqa: F401  (fails loudly if not built)
+
+    wl = make_config(args.workload)
+    print(f"bench: workload {wl.name}, building rotating copies", file=sys.stderr, flush=True)
+    m = measure(torch, wl, args.steps, args.warmup)
+    cost = m["cost"]
+    ms = m["gpu_ms"] / args.steps
+    tok_s = wl.n / (ms * 1e-3)
+    gbps = cost["bytes"] / (ms * 1e-3) / 1e9
+    print(f"bench: {ms * 1e3:.2f} us/forward, {gbps:.0f} GB/s", file=sys.stderr, flush=True)
+
+    # dominant kernel roofline
+    kern = m["kernels"]
+    dom = max(kern.items(), key=lambda kv: kv[1]["total_ms"])[0] if kern else None
+    roof = None
+    if dom is not None:
+        k = kern[dom]
+        avg_s = k["total_ms"] / max(1, k["launches"]) * 1e-3
+        kb = dominant_kernel_bytes(dom, wl, cost)
+        if kb is not None:
+            ach = kb / avg_s / 1e9
+            roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 3),
+                    "bytes_per_launch": kb}
+
+    extra = {"gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+             "bytes_per_forward": cost["bytes"], "adapter_bytes": cost["adapter_bytes"],
+             "flops_per_forward": cost["flops"], "launches_per_forward": cost["launches"],
+             "kernels_us": {k: round(v["total_ms"] / max(1, v["launches"]) * 1e3, 3)
+                            for k, v in kern.items()},
+             "rotating_sets": m["n_sets"], "wall_s": round(m["wall"], 4)}
+    del m
+
+    if not args.no_overhead and args.workload == 2:
+        wl1 = make_config(1)
+        print("bench: all-LoRA comparison workload", file=sys.stderr, flush=True)
+        m1 = measure(torch, wl1, args.steps, args.warmup)
+        ms1 = m1["gpu_ms"] / args.steps
+        extra["all_lora_us"] = round(ms1 * 1e3, 3)
+        extra["all_lora_gbps"] = round(m1["cost"]["bytes"] / (ms1 * 1e-3) / 1e9, 1)
+        extra["mixed_over_all_lora_time"] = round(ms / ms1, 4)
+        del m1
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    out = {"metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+           "data": "synthetic (seeded; shapes and distributions of the named workload)",
+           "config": {"workload": wl.name, "tokens": wl.n, "d_in": wl.d_in, "d_out": wl.d_out,
+                      "adapters": len(wl.adapters), "seed": wl.seed},
+           "roofline": roof, "cpu_baseline": cpu, "extra": extra}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

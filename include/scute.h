@@ -1,0 +1,276 @@
+/*
+ * scute.h - C ABI of the normal-form batched adapter layer on MI355X (gfx950).
+ *
+ * The layer computes, for every token t of a batch whose tokens belong to
+ * many adapters a = a(t) over one shared base weight W,
+ *
+ *   y_t = ((x_t R_a) W) (.) s_a + b_a + sum_k c_k (((x_t A_k) (.) d_k) B_k (.) e_k)
+ *
+ * (row vectors; "The big picture: six extra slots in the LoRA computation",
+ * paper-daily.com explainer of "Scute: Exact Batched Serving for PEFT
+ * Adapters Beyond LoRA"). LoRA, DoRA, (IA)^3, VeRA and OFT adapters are all
+ * written in this normal form ("What problem is it solving?").
+ *
+ * Buffer conventions (PyTorch nn.Linear layout; the formula uses transposes):
+ *   x     [n][d_in]    activation dtype, row-major
+ *   W     [d_out][d_in] activation dtype, row-major (K contiguous)
+ *   y     [n][d_out]   float32
+ *   A     [rank][d_in]   B [d_out][rank]
+ *   A_sh  [r_v][d_in]    B_sh [d_out][r_v]
+ *   Q, R  [d_in/blk][blk][blk], block kb maps input i -> output j via
+ *         out[kb*blk + j] = sum_i in[kb*blk + i] * M[kb][i][j]
+ *
+ * Errors: every call returns a scute_status; 0 is success. On failure a
+ * thread-local message is available from scute_last_error() and the object
+ * passed in is left as it was (still usable). No C++ exception crosses this
+ * boundary. Device-side faults of asynchronous calls surface at the caller's
+ * next synchronisation of the stream.
+ *
+ * Threading: one layer may run forwards on one stream at a time. Loads and
+ * unloads must not overlap a forward on the same layer; the caller
+ * serialises them.
+ */
+#ifndef SCUTE_H
+#define SCUTE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t scute_status;
+
+#define SCUTE_OK 0
+#define SCUTE_E_INVALID (-1)     /* null pointer or bad argument value        */
+#define SCUTE_E_SHAPE (-2)       /* sizes inconsistent with the layer         */
+#define SCUTE_E_NOMEM (-3)       /* allocation failed or capacity exhausted   */
+#define SCUTE_E_HIP (-4)         /* HIP runtime error                         */
+#define SCUTE_E_STATE (-5)       /* wrong state: id occupied / not loaded,
+                                    stale plan, shared VeRA pair not set      */
+#define SCUTE_E_UNSUPPORTED (-6) /* valid request this build does not serve   */
+
+typedef enum scute_dtype {
+  SCUTE_F32 = 0,
+  SCUTE_BF16 = 1, /* stored as uint16 bit patterns */
+  SCUTE_F64 = 2
+} scute_dtype;
+
+typedef enum scute_method {
+  SCUTE_LORA = 0,       /* y = xW + b + c (xA) B                                 */
+  SCUTE_DORA = 1,       /* y = x W_D + b, W_D = (W + cAB) diag(m / colnorm(W+cAB)) */
+  SCUTE_IA3 = 2,        /* y = (xW) (.) l + b  (l on the s slot)                 */
+  SCUTE_VERA = 3,       /* y = xW + b + (((x A_sh) (.) d) B_sh) (.) (c e)        */
+  SCUTE_OFT = 4,        /* y = (x R) W + b, R = blockdiag(Cayley(Q_k))           */
+  SCUTE_NORMAL_FORM = 5 /* slots given directly: R, s, b, one own term, VeRA term */
+} scute_method;
+
+typedef struct scute_layer scute_layer;
+typedef struct scute_batch scute_batch;
+
+/*
+ * One adapter as it comes from its method ("How does Scute plug into vLLM?":
+ * the converter rewrites each checkpoint in the normal form at load).
+ * Every array is a HOST pointer in `dtype` (SCUTE_F64, SCUTE_F32, or
+ * SCUTE_BF16 as uint16). Arrays a method does not use are ignored; an
+ * optional array left null takes its identity value (ones, zero, identity).
+ */
+typedef struct scute_adapter_desc {
+  int32_t method; /* scute_method                                            */
+  int32_t dtype;  /* element type of the host arrays below                   */
+  int32_t rank;   /* rank r of the own low-rank term (LoRA, DoRA, NORMAL_FORM
+                     with A and B); 0 = no own term                          */
+  int32_t blk;    /* block size of Q (OFT) or R (NORMAL_FORM); divides d_in  */
+  double c;       /* scalar c: of the own term (LoRA, DoRA, NORMAL_FORM), or
+                     of the shared term (VeRA; the pages' VeRA uses c = 1)   */
+  const void* A;  /* [rank][d_in]   own down factor                          */
+  const void* B;  /* [d_out][rank]  own up factor                            */
+  const void* d;  /* [rank]   NORMAL_FORM own-term d (null: ones)            */
+  const void* e;  /* [d_out]  NORMAL_FORM own-term e (null: ones)            */
+  const void* m;  /* [d_out]  DoRA learned column lengths                    */
+  const void* l;  /* [d_out]  (IA)^3 vector                                  */
+  const void* vd; /* [r_v]    VeRA d (VERA; NORMAL_FORM shared term)         */
+  const void* ve; /* [d_out]  VeRA e                                         */
+  const void* Q;  /* [d_in/blk][blk][blk] OFT skew-symmetric blocks          */
+  const void* R;  /* [d_in/blk][blk][blk] NORMAL_FORM rotation blocks        */
+  const void* s;  /* [d_out]  NORMAL_FORM s (null: ones)                     */
+  const void* b;  /* [d_out]  shift b, any method (null: zero)               */
+} scute_adapter_desc;
+
+/* Per-batch algorithmic cost (the byte / FLOP model; "Where is the cheapest
+ * place to compute the remaining slots?": adapter work is priced in bytes,
+ * added time = extra bytes / bandwidth + extra launches x launch cost). */
+typedef struct scute_cost {
+  double bytes;         /* x + W + y + every touched adapter's stored factors
+                           + shared VeRA pair once if any VeRA row           */
+  double adapter_bytes; /* bytes minus x, W and y                            */
+  double flops;         /* 2 n d_in d_out + own terms + VeRA terms + rotations */
+  double base_flops;    /* 2 n d_in d_out                                    */
+  int32_t launches;     /* kernel launches per forward                       */
+  int32_t n_tokens;
+  int32_t n_segments;   /* runs of one adapter after the stable sort         */
+  int32_t n_rot_rows;   /* rows with a rotation slot (OFT)                   */
+  int32_t n_vera_rows;  /* rows with a shared VeRA term                      */
+  int32_t n_touched;    /* distinct adapters with at least one token         */
+} scute_cost;
+
+/* Create a layer context for one (d_in, d_out, activation dtype, device).
+ * device >= 0: HIP device ordinal; every forward runs there.
+ * device == -1: host-only context (fold, plan and cost model only; the
+ *   forward returns SCUTE_E_UNSUPPORTED). Used to test host logic without a
+ *   GPU.
+ * act_dtype: SCUTE_BF16 (bf16 inputs, fp32 accumulate) or SCUTE_F32.
+ * max_adapters: adapter ids run 0 .. max_adapters-1.
+ * The library owns everything it allocates; release with scute_layer_destroy. */
+scute_status scute_layer_create(int32_t device, int64_t d_in, int64_t d_out,
+                                int32_t act_dtype, int32_t max_adapters,
+                                scute_layer** out);
+
+/* Free the layer and every adapter it holds. The caller must have
+ * synchronised every stream that used it. Plans built for it become invalid
+ * and must still be destroyed. Null is accepted. */
+scute_status scute_layer_destroy(scute_layer* layer);
+
+/* Set the shared VeRA pair ("Which slots can be merged at load?": VeRA's A
+ * and B are shared by every VeRA tenant, so d and e stay live; "How does
+ * Scute plug into vLLM?": VeRA keeps a reference to the shared matrices).
+ * A_sh [r_v][d_in] and B_sh [d_out][r_v] are DEVICE pointers in the
+ * activation dtype, BORROWED: the caller keeps them alive and unchanged
+ * while the layer is used. Must precede loading any adapter with a VeRA
+ * term; may be replaced only while no VeRA adapter is loaded.
+ * Host-only layers accept host pointers (not dereferenced). */
+scute_status scute_set_vera_shared(scute_layer* layer, const void* A_sh,
+                                   const void* B_sh, int32_t r_v);
+
+/* Load adapter `id`: fold its slots ("Which slots can be merged at load?":
+ * a slot next to a factor the adapter owns merges into it, a slot next to
+ * shared W or the shared VeRA pair stays live), in fp64 on the host, then
+ * store the folded factors in library-owned device memory:
+ *   own term:  A' = c A diag(d), B' = B diag(e)  (activation dtype)
+ *   DoRA:      s = m / colnorm(W + cAB) stays live on the base path and
+ *              also folds into B' (e = s), c folds into A'
+ *   (IA)^3:    s = l live     VeRA: d, c e live     OFT: P = R - I
+ *   s, b, VeRA d and e are stored in float32.
+ * W_host ([d_out][d_in] in desc->dtype, HOST pointer) is read only for
+ * DoRA and may be null otherwise. `stream` orders the uploads (null: the
+ * default stream); the call returns after they complete.
+ * Errors: SCUTE_E_STATE if `id` is occupied or the VeRA pair is missing,
+ * SCUTE_E_SHAPE for a bad rank / block size, SCUTE_E_INVALID for a missing
+ * array, SCUTE_E_NOMEM if device memory runs out. */
+scute_status scute_load_adapter(scute_layer* layer, int32_t id,
+                                const scute_adapter_desc* desc,
+                                const void* W_host, void* stream);
+
+/* Unload adapter `id` and free its memory after `stream` drains.
+ * SCUTE_E_STATE if `id` is not loaded. Plans built before become stale. */
+scute_status scute_unload_adapter(scute_layer* layer, int32_t id, void* stream);
+
+/* Build the batch plan from a HOST array token_adapter[n] (-1: base path
+ * only): a stable sort of tokens by adapter so that every run of rows
+ * belongs to one adapter ("Where is the cheapest place...": each tile of
+ * the expand belongs to one adapter; each row looks up its tenant's VeRA
+ * vectors and rotation). Rows with a rotation slot come first, then rows
+ * with a shared VeRA term, then the rest, each group ordered by adapter id
+ * and token index. The plan is library-owned, sized workspaces included,
+ * and may be reused for any number of forwards with the same assignment
+ * until the layer's adapters change. n may be 0.
+ * Errors: SCUTE_E_STATE if a token names an id that is not loaded. */
+scute_status scute_plan_batch(scute_layer* layer, const int32_t* token_adapter,
+                              int32_t n, void* stream, scute_batch** out);
+
+/* Free a plan (after the streams that used it are synchronised). Null ok. */
+scute_status scute_batch_destroy(scute_batch* batch);
+
+/* The forward pass on `stream` (null: default stream), asynchronous.
+ * x [n][d_in] and W [d_out][d_in] are DEVICE pointers in the activation
+ * dtype; y [n][d_out] is a DEVICE float32 pointer that is fully written.
+ * All three are borrowed for the call. Every step runs in this library's
+ * HIP kernels: OFT rotation, base GEMM with the s / b epilogue, own-term
+ * shrink and expand, and the whole-batch shared VeRA term ("How does Scute
+ * plug into vLLM?": four steps, the rotation before the GEMM).
+ * Errors: SCUTE_E_STATE if the plan is stale or from another layer,
+ * SCUTE_E_UNSUPPORTED on a host-only layer, SCUTE_E_INVALID for null or
+ * misaligned pointers (16-byte alignment required). */
+scute_status scute_layer_forward(scute_layer* layer, const scute_batch* batch,
+                                 const void* x, const void* W, float* y,
+                                 void* stream);
+
+/* Algorithmic bytes / FLOPs / launches of one forward with this plan. */
+scute_status scute_cost_model(const scute_layer* layer, const scute_batch* batch,
+                              scute_cost* out);
+
+/* ---- introspection (tests, debugging) ---------------------------------- */
+
+typedef enum scute_slot {
+  SCUTE_SLOT_A = 0,  /* folded A' [rank][d_in]        activation dtype */
+  SCUTE_SLOT_B = 1,  /* folded B' [d_out][rank]       activation dtype */
+  SCUTE_SLOT_S = 2,  /* live s [d_out]                float32          */
+  SCUTE_SLOT_BIAS = 3, /* b [d_out]                   float32          */
+  SCUTE_SLOT_VD = 4, /* VeRA d [r_v]                  float32          */
+  SCUTE_SLOT_VE = 5, /* VeRA e, c folded [d_out]      float32          */
+  SCUTE_SLOT_P = 6   /* R - I [d_in/blk][blk][blk]    activation dtype */
+} scute_slot;
+
+typedef struct scute_adapter_info {
+  int32_t loaded;
+  int32_t method;
+  int32_t rank;
+  int32_t blk;
+  int32_t has_R, has_s, has_b, has_term, has_vera;
+} scute_adapter_info;
+
+scute_status scute_adapter_info_get(const scute_layer* layer, int32_t id,
+                                    scute_adapter_info* out);
+
+/* Copy one stored slot of adapter `id` to HOST memory `dst` of `dst_bytes`
+ * bytes (must be exactly the slot's size). SCUTE_E_STATE if the adapter
+ * does not hold that slot. */
+scute_status scute_read_slot(const scute_layer* layer, int32_t id, int32_t slot,
+                             void* dst, int64_t dst_bytes);
+
+typedef struct scute_batch_info {
+  int32_t n;
+  int32_t n_segments;
+  int32_t n_rot_rows;  /* rows 0 .. n_rot_rows-1 of the sorted order rotate */
+  int32_t n_vera_rows;
+  int32_t max_rank;
+} scute_batch_info;
+
+scute_status scute_batch_info_get(const scute_batch* batch, scute_batch_info* out);
+
+/* Copy the plan's tables to HOST memory:
+ *   perm[n]            token index at each sorted position
+ *   seg[3*n_segments]  (adapter id, first sorted position, length) per run
+ * Either pointer may be null. */
+scute_status scute_batch_read(const scute_batch* batch, int32_t* perm, int32_t* seg);
+
+/* ---- kernel timing (instrumentation) ------------------------------------ */
+
+/* When enabled, every forward on this layer records a HIP event pair around
+ * each of its kernel launches, on the forward's stream. Timings accumulate
+ * per kernel name until read. Costs a little launch overhead; off by default. */
+scute_status scute_profile_enable(scute_layer* layer, int32_t enable);
+
+typedef struct scute_kernel_time {
+  char name[32];     /* kernel role, e.g. "gemm"                           */
+  int32_t launches;  /* launches timed since the last read                 */
+  double total_ms;   /* summed event-to-event time of those launches       */
+} scute_kernel_time;
+
+/* Wait for the recorded events, write up to `capacity` per-kernel totals to
+ * HOST memory `out`, set *count to the number of kernel names, and reset
+ * the totals. */
+scute_status scute_profile_read(scute_layer* layer, scute_kernel_time* out, int32_t capacity,
+                                int32_t* count);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* scute_last_error(void);
+
+/* Library version string. */
+const char* scute_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCUTE_H */

@@ -1,0 +1,386 @@
+// The forward pass: OFT rotation, shrink, base GEMM with the s / b
+// epilogue, expand and the shared VeRA term.
+//
+// Order of steps ("How does Scute plug into vLLM?" and "Where is the
+// cheapest place to compute the remaining slots?", paper-daily.com explainer
+// of "Scute: Exact Batched Serving for PEFT Adapters Beyond LoRA"): the
+// rotation runs in its own pass before the shared GEMM; the base GEMM runs
+// once for the whole batch; the own low-rank term is shrunk and expanded per
+// adapter; s multiplies the base output and the low-rank update is added
+// unscaled; the shared VeRA term is computed for every VeRA row of the batch
+// with the shared pair read once per step.
+//
+// Rotation: x R = x + x (R - I). The library stores P = R - I and computes
+// delta = x P in fp32, rounded once to the activation dtype, then feeds both
+// x and delta through the same W. Rounding only the small delta keeps the
+// rotation's effect accurate in bf16, where rounding x R itself would not.
+//
+// This file holds the generic kernels: correct for every shape the ABI
+// accepts, in fp32 or bf16, with fp32 accumulation.
+
+#include <string.h>
+
+#include "internal.h"
+
+namespace scute {
+
+__device__ __forceinline__ float ldf(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ldf(const uint16_t* p, size_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+__device__ __forceinline__ void stf(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void stf(uint16_t* p, size_t i, float v) {
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFu + ((u >> 16) & 1u);  // round to nearest even (finite inputs)
+  p[i] = (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// rotation: delta[p][col] = sum_i x[perm[p]][kb*blk + i] * P[kb][i][col - kb*blk]
+// grid (ceil(d_in / 256), n_rot)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_rotate_ref(const T* __restrict__ x,
+                                                    const int32_t* __restrict__ perm,
+                                                    const int32_t* __restrict__ row_adapter,
+                                                    const SlotEntry* __restrict__ table,
+                                                    int64_t d_in, T* __restrict__ delta) {
+  const int32_t p = blockIdx.y;
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= d_in) return;
+  const SlotEntry E = table[row_adapter[p]];
+  const int32_t blk = E.blk;
+  const int64_t kb = col / blk, jj = col - kb * blk;
+  const T* xr = x + (size_t)perm[p] * d_in + kb * blk;
+  const T* P = (const T*)E.P + (size_t)kb * blk * blk;
+  float acc = 0.f;
+  for (int32_t i = 0; i < blk; ++i) acc += ldf(xr, i) * ldf(P, (size_t)i * blk + jj);
+  stf(delta, (size_t)p * d_in + col, acc);
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  if (threadIdx.x == 0) s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// own-term shrink: t[p][k] = x[perm[p]] . A'[k]   (0 for k >= rank)
+// grid (max_rank, n), 256 threads reduce over d_in
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_shrink_ref(const T* __restrict__ x,
+                                                    const int32_t* __restrict__ perm,
+                                                    const int32_t* __restrict__ row_adapter,
+                                                    const SlotEntry* __restrict__ table,
+                                                    int64_t d_in, int32_t max_rank,
+                                                    float* __restrict__ t) {
+  __shared__ float red[4];
+  const int32_t p = blockIdx.y, k = blockIdx.x;
+  const int32_t a = row_adapter[p];
+  bool live = false;
+  SlotEntry E{};
+  if (a >= 0) {
+    E = table[a];
+    live = (E.flags & F_TERM) && k < E.rank;
+  }
+  if (!live) {
+    if (threadIdx.x == 0) t[(size_t)p * max_rank + k] = 0.f;
+    return;
+  }
+  const T* xr = x + (size_t)perm[p] * d_in;
+  const T* Ar = (const T*)E.A + (size_t)k * d_in;
+  float acc = 0.f;
+  for (int64_t i = threadIdx.x; i < d_in; i += 256) acc += ldf(xr, i) * ldf(Ar, i);
+  acc = block_sum_256(acc, red);
+  if (threadIdx.x == 0) t[(size_t)p * max_rank + k] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// VeRA shrink over the whole batch: u[p][k] = d_a[k] * (x[perm[p]] . A_sh[k])
+// for every VeRA row p = vera_pos[v]; grid (r_v, n_vera)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_vera_shrink_ref(const T* __restrict__ x,
+                                                         const int32_t* __restrict__ perm,
+                                                         const int32_t* __restrict__ row_adapter,
+                                                         const int32_t* __restrict__ vera_pos,
+                                                         const SlotEntry* __restrict__ table,
+                                                         const T* __restrict__ A_sh, int64_t d_in,
+                                                         int32_t r_v, float* __restrict__ u) {
+  __shared__ float red[4];
+  const int32_t k = blockIdx.x;
+  const int32_t p = vera_pos[blockIdx.y];
+  const SlotEntry E = table[row_adapter[p]];
+  const T* xr = x + (size_t)perm[p] * d_in;
+  const T* Ar = A_sh + (size_t)k * d_in;
+  float acc = 0.f;
+  for (int64_t i = threadIdx.x; i < d_in; i += 256) acc += ldf(xr, i) * ldf(Ar, i);
+  acc = block_sum_256(acc, red);
+  if (threadIdx.x == 0) u[(size_t)p * r_v + k] = acc * E.vd[k];
+}
+
+// ---------------------------------------------------------------------------
+// base GEMM with epilogue, 32x32 output tile per block, LDS-staged operands:
+//   y[perm[p]][j] = (x[perm[p]] . W[j] + [p < n_rot] delta[p] . W[j]) * s[j] + b[j]
+// grid (ceil(d_out/32), ceil(n/32)), 256 threads, 4 outputs per thread
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const T* __restrict__ W,
+                                                  const T* __restrict__ delta,
+                                                  const int32_t* __restrict__ perm,
+                                                  const int32_t* __restrict__ row_adapter,
+                                                  const SlotEntry* __restrict__ table, int32_t n,
+                                                  int32_t n_rot, int64_t d_in, int64_t d_out,
+                                                  float* __restrict__ y) {
+  __shared__ float xs[32][33];
+  __shared__ float ws[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const int32_t p0 = blockIdx.y * 32;
+  const int64_t j0 = (int64_t)blockIdx.x * 32;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int passes = (p0 < n_rot) ? 2 : 1;
+  for (int pass = 0; pass < passes; ++pass) {
+    for (int64_t k0 = 0; k0 < d_in; k0 += 32) {
+      for (int q = 0; q < 4; ++q) {
+        const int r = ty + 8 * q;
+        const int32_t p = p0 + r;
+        const int64_t kk = k0 + tx;
+        float xv = 0.f;
+        if (kk < d_in) {
+          if (pass == 0) {
+            if (p < n) xv = ldf(x, (size_t)perm[p] * d_in + kk);
+          } else {
+            if (p < n_rot) xv = ldf(delta, (size_t)p * d_in + kk);
+          }
+        }
+        xs[r][tx] = xv;
+        const int64_t j = j0 + r;
+        ws[r][tx] = (j < d_out && kk < d_in) ? ldf(W, (size_t)j * d_in + kk) : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 8
+      for (int kk = 0; kk < 32; ++kk) {
+        const float wv = ws[tx][kk];
+        for (int q = 0; q < 4; ++q) acc[q] += xs[ty + 8 * q][kk] * wv;
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t j = j0 + tx;
+  if (j >= d_out) return;
+  for (int q = 0; q < 4; ++q) {
+    const int32_t p = p0 + ty + 8 * q;
+    if (p >= n) continue;
+    float v = acc[q];
+    const int32_t a = row_adapter[p];
+    if (a >= 0) {
+      const SlotEntry E = table[a];
+      if (E.flags & F_S) v *= E.s[j];
+      if (E.flags & F_B) v += E.b[j];
+    }
+    y[(size_t)perm[p] * d_out + j] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// expand: y[perm[p]][j] += t[p] . B'[j] + e_a[j] * (u[p] . B_sh[j])
+// grid (ceil(d_out/256), n)
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) k_expand_ref(const float* __restrict__ t,
+                                                    const float* __restrict__ u,
+                                                    const T* __restrict__ B_sh,
+                                                    const int32_t* __restrict__ perm,
+                                                    const int32_t* __restrict__ row_adapter,
+                                                    const SlotEntry* __restrict__ table,
+                                                    int32_t max_rank, int32_t r_v, int64_t d_out,
+                                                    float* __restrict__ y) {
+  const int32_t p = blockIdx.y;
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= d_out) return;
+  const int32_t a = row_adapter[p];
+  if (a < 0) return;
+  const SlotEntry E = table[a];
+  float v = 0.f;
+  if (E.flags & F_TERM) {
+    const T* Bj = (const T*)E.B + (size_t)j * E.rank;
+    const float* tp = t + (size_t)p * max_rank;
+    for (int32_t k = 0; k < E.rank; ++k) v += tp[k] * ldf(Bj, k);
+  }
+  if (E.flags & F_VERA) {
+    const T* Bj = B_sh + (size_t)j * r_v;
+    const float* up = u + (size_t)p * r_v;
+    float w = 0.f;
+    for (int32_t k = 0; k < r_v; ++k) w += up[k] * ldf(Bj, k);
+    v += E.ve[j] * w;
+  }
+  if (E.flags & (F_TERM | F_VERA)) y[(size_t)perm[p] * d_out + j] += v;
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+
+static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+// Kernel timing: when the layer has profiling on, bracket each launch with a
+// HIP event pair on the launch stream.
+struct ProfScope {
+  scute_layer* L;
+  hipStream_t st;
+  ProfEvent ev{};
+  bool on = false;
+  ProfScope(scute_layer* L_, hipStream_t st_, const char* name) : L(L_), st(st_) {
+    if (!L->profiling) return;
+    int32_t kind = -1;
+    for (size_t i = 0; i < L->prof_names.size(); ++i)
+      if (L->prof_names[i] == name) kind = (int32_t)i;
+    if (kind < 0) {
+      kind = (int32_t)L->prof_names.size();
+      L->prof_names.push_back(name);
+      L->prof_ms.push_back(0.0);
+      L->prof_count.push_back(0);
+    }
+    ev.kind = kind;
+    for (hipEvent_t* e : {&ev.start, &ev.stop}) {
+      if (!L->prof_pool.empty()) {
+        *e = L->prof_pool.back();
+        L->prof_pool.pop_back();
+      } else if (hipEventCreate(e) != hipSuccess) {
+        return;
+      }
+    }
+    on = hipEventRecord(ev.start, st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    if (hipEventRecord(ev.stop, st) == hipSuccess) L->prof_pending.push_back(ev);
+  }
+};
+
+template <typename T>
+static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x, const T* W,
+                               float* y, hipStream_t st, int32_t* launches) {
+  const int32_t n = B->n;
+  const int64_t d_in = L->d_in, d_out = L->d_out;
+  int32_t nl = 0;
+  if (B->n_rot > 0) {
+    ProfScope ps(L, st, "rotate");
+    hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), B->n_rot), dim3(256), 0, st, x,
+                       B->d_perm, B->d_row_adapter, L->table_dev, d_in, (T*)B->delta);
+    ++nl;
+  }
+  if (B->max_rank > 0) {
+    ProfScope ps(L, st, "shrink");
+    hipLaunchKernelGGL(k_shrink_ref<T>, dim3(B->max_rank, n), dim3(256), 0, st, x, B->d_perm,
+                       B->d_row_adapter, L->table_dev, d_in, B->max_rank, B->t);
+    ++nl;
+  }
+  if (B->n_vera > 0) {
+    ProfScope ps(L, st, "vera_shrink");
+    hipLaunchKernelGGL(k_vera_shrink_ref<T>, dim3(L->r_v, B->n_vera), dim3(256), 0, st, x,
+                       B->d_perm, B->d_row_adapter, B->d_vera_pos, L->table_dev,
+                       (const T*)L->A_sh, d_in, L->r_v, B->u);
+    ++nl;
+  }
+  {
+    ProfScope ps(L, st, "gemm");
+    hipLaunchKernelGGL(k_gemm_ref<T>, dim3(cdiv(d_out, 32), cdiv(n, 32)), dim3(256), 0, st, x, W,
+                       (const T*)B->delta, B->d_perm, B->d_row_adapter, L->table_dev, n,
+                       B->n_rot, d_in, d_out, y);
+    ++nl;
+  }
+  if (B->max_rank > 0 || B->n_vera > 0) {
+    ProfScope ps(L, st, "expand");
+    hipLaunchKernelGGL(k_expand_ref<T>, dim3(cdiv(d_out, 256), n), dim3(256), 0, st, B->t, B->u,
+                       (const T*)L->B_sh, B->d_perm, B->d_row_adapter, L->table_dev, B->max_rank,
+                       L->r_v, d_out, y);
+    ++nl;
+  }
+  SCUTE_HIP_CHECK(hipGetLastError());
+  if (launches) *launches = nl;
+  return SCUTE_OK;
+}
+
+int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
+  (void)L;
+  if (B->n == 0) return 0;
+  return (B->n_rot > 0) + (B->max_rank > 0) + (B->n_vera > 0) + 1 +
+         (B->max_rank > 0 || B->n_vera > 0);
+}
+
+scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x, const void* W,
+                            float* y, hipStream_t st, int32_t* launches) {
+  if (L->act == SCUTE_BF16)
+    return launch_ref<uint16_t>(L, B, (const uint16_t*)x, (const uint16_t*)W, y, st, launches);
+  return launch_ref<float>(L, B, (const float*)x, (const float*)W, y, st, launches);
+}
+
+}  // namespace scute
+
+using namespace scute;
+
+extern "C" scute_status scute_layer_forward(scute_layer* L, const scute_batch* B, const void* x,
+                                            const void* W, float* y, void* stream) {
+  if (!L || !B) return fail(SCUTE_E_INVALID, "scute_layer_forward: null layer or plan");
+  if (B->layer != L) return fail(SCUTE_E_STATE, "scute_layer_forward: plan belongs to another layer");
+  if (B->epoch != L->epoch)
+    return fail(SCUTE_E_STATE, "scute_layer_forward: plan is stale (adapters changed since planning)");
+  if (L->device < 0)
+    return fail(SCUTE_E_UNSUPPORTED, "scute_layer_forward: host-only layer has no forward");
+  if (B->n == 0) return SCUTE_OK;
+  if (!x || !W || !y) return fail(SCUTE_E_INVALID, "scute_layer_forward: null x, W or y");
+  if (((uintptr_t)x | (uintptr_t)W | (uintptr_t)y) & 15)
+    return fail(SCUTE_E_INVALID, "scute_layer_forward: x, W and y must be 16-byte aligned");
+  if (B->n_vera > 0 && (!L->A_sh || !L->B_sh))
+    return fail(SCUTE_E_STATE, "scute_layer_forward: shared VeRA pair not set");
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  if (prev != L->device) (void)hipSetDevice(L->device);
+  scute_status st = launch_forward(L, B, x, W, y, (hipStream_t)stream, nullptr);
+  if (prev != L->device && prev >= 0) (void)hipSetDevice(prev);
+  return st;
+}
+
+extern "C" scute_status scute_profile_enable(scute_layer* L, int32_t enable) {
+  if (!L) return fail(SCUTE_E_INVALID, "scute_profile_enable: layer is null");
+  if (L->device < 0 && enable)
+    return fail(SCUTE_E_UNSUPPORTED, "scute_profile_enable: host-only layer");
+  L->profiling = enable != 0;
+  return SCUTE_OK;
+}
+
+extern "C" scute_status scute_profile_read(scute_layer* L, scute_kernel_time* out,
+                                           int32_t capacity, int32_t* count) {
+  if (!L || !count) return fail(SCUTE_E_INVALID, "scute_profile_read: null argument");
+  if (capacity > 0 && !out) return fail(SCUTE_E_INVALID, "scute_profile_read: out is null");
+  for (const ProfEvent& ev : L->prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(ev.stop) == hipSuccess &&
+        hipEventElapsedTime(&ms, ev.start, ev.stop) == hipSuccess) {
+      L->prof_ms[ev.kind] += ms;
+      L->prof_count[ev.kind] += 1;
+    }
+    L->prof_pool.push_back(ev.start);
+    L->prof_pool.push_back(ev.stop);
+  }
+  L->prof_pending.clear();
+  *count = (int32_t)L->prof_names.size();
+  for (int32_t i = 0; i < *count && i < capacity; ++i) {
+    memset(out[i].name, 0, sizeof(out[i].name));
+    strncpy(out[i].name, L->prof_names[i].c_str(), sizeof(out[i].name) - 1);
+    out[i].launches = L->prof_count[i];
+    out[i].total_ms = L->prof_ms[i];
+  }
+  for (size_t i = 0; i < L->prof_ms.size(); ++i) {
+    L->prof_ms[i] = 0.0;
+    L->prof_count[i] = 0;
+  }
+  return SCUTE_OK;
+}

@@ -1,0 +1,124 @@
+// Internal definitions shared by the host runtime and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/scute.h"
+
+namespace scute {
+
+// flags of one adapter's live-slot entry
+enum : int32_t {
+  F_LOADED = 1,
+  F_R = 2,     // rotation slot (P = R - I stored)
+  F_S = 4,     // live s
+  F_B = 8,     // shift b
+  F_TERM = 16, // own low-rank term (A', B')
+  F_VERA = 32, // shared VeRA term (d, e live)
+};
+
+// Device-visible live-slot entry of one adapter (struct of pointers into
+// the adapter's library-owned storage). Unused pointers are null.
+struct SlotEntry {
+  const void* A;   // A' [rank][d_in]   act dtype
+  const void* B;   // B' [d_out][rank]  act dtype
+  const void* P;   // R - I [d_in/blk][blk][blk] act dtype
+  const float* s;  // [d_out]
+  const float* b;  // [d_out]
+  const float* vd; // [r_v]
+  const float* ve; // [d_out]
+  int32_t rank;
+  int32_t blk;
+  int32_t flags;
+  int32_t method;
+};
+
+struct AdapterStore {
+  void* mem = nullptr;  // one allocation holding every slot (device or host)
+  size_t bytes = 0;
+  size_t off[7] = {0, 0, 0, 0, 0, 0, 0};  // offsets per scute_slot
+  size_t len[7] = {0, 0, 0, 0, 0, 0, 0};  // byte sizes per scute_slot
+};
+
+}  // namespace scute
+
+namespace scute {
+struct ProfEvent {
+  int32_t kind;
+  hipEvent_t start, stop;
+};
+}  // namespace scute
+
+struct scute_layer {
+  int32_t device = -1;
+  int64_t d_in = 0, d_out = 0;
+  int32_t act = SCUTE_BF16;
+  int32_t max_adapters = 0;
+  std::vector<scute::SlotEntry> table;  // host mirror
+  std::vector<scute::AdapterStore> store;
+  scute::SlotEntry* table_dev = nullptr;
+  const void* A_sh = nullptr;
+  const void* B_sh = nullptr;
+  int32_t r_v = 0;
+  int32_t n_vera_loaded = 0;
+  uint64_t epoch = 1;  // bumps on every load / unload
+  int32_t num_cu = 0;
+  // kernel timing (scute_profile_enable)
+  bool profiling = false;
+  std::vector<scute::ProfEvent> prof_pending;
+  std::vector<hipEvent_t> prof_pool;
+  std::vector<std::string> prof_names;
+  std::vector<double> prof_ms;
+  std::vector<int32_t> prof_count;
+};
+
+struct scute_batch {
+  const scute_layer* layer = nullptr;
+  uint64_t epoch = 0;
+  int32_t n = 0;
+  int32_t n_rot = 0;      // sorted positions [0, n_rot) carry a rotation
+  int32_t n_vera = 0;     // rows with a VeRA term
+  int32_t max_rank = 0;   // largest own-term rank among touched adapters
+  int32_t n_touched = 0;
+  // host tables
+  std::vector<int32_t> perm;         // [n] token at sorted position
+  std::vector<int32_t> row_adapter;  // [n] adapter of sorted position (-1)
+  std::vector<int32_t> seg;          // [3 * nseg] (adapter, start, len)
+  std::vector<int32_t> vera_pos;     // [n_vera] sorted positions with VeRA
+  // device copies (one allocation) and workspaces
+  void* dev = nullptr;
+  int32_t* d_perm = nullptr;
+  int32_t* d_row_adapter = nullptr;
+  int32_t* d_seg = nullptr;
+  int32_t* d_vera_pos = nullptr;
+  void* ws = nullptr;         // workspace allocation
+  void* delta = nullptr;      // [n_rot][d_in] act dtype: x (R - I)
+  float* t = nullptr;         // [n][max_rank]  own-term shrink
+  float* u = nullptr;         // [n][r_v] VeRA shrink scaled by d (rows with VeRA)
+  int32_t nseg() const { return (int32_t)(seg.size() / 3); }
+};
+
+namespace scute {
+
+// error reporting (thread-local message)
+scute_status fail(scute_status code, const std::string& msg);
+scute_status hip_fail(hipError_t e, const char* what);
+#define SCUTE_HIP_CHECK(expr)                                   \
+  do {                                                          \
+    hipError_t _e = (expr);                                     \
+    if (_e != hipSuccess) return ::scute::hip_fail(_e, #expr);  \
+  } while (0)
+
+size_t dtype_size(int32_t dt);
+
+// forward launcher (forward.hip)
+scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x,
+                            const void* W, float* y, hipStream_t stream,
+                            int32_t* launches_out);
+int32_t forward_launch_count(const scute_layer* L, const scute_batch* B);
+
+}  // namespace scute
