@@ -93,6 +93,14 @@ SIGNATURES = {
 
 
 def _load():
+    # One HIP runtime per process: PyTorch ships its own libamdhip64 (soname
+    # libamdhip64.so.7). Importing torch first makes the dynamic loader bind
+    # libscute.so to that same runtime, so device pointers and streams from
+    # torch are valid in the library's calls.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m lora_normal_form_amd.build` (hipcc, gfx950)")
