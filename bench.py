@@ -94,11 +94,18 @@ def time_forwards(torch, sets, steps, warmup, profile=False):
 
 
 def dominant_kernel_bytes(name, wl, cost):
-    """Algorithmic bytes one launch of kernel ``name`` must move."""
+    """Algorithmic bytes one launch of kernel ``name`` must move.
+
+    decode_main (base GEMM + fused expand): x, W, y, touched adapters' B', s,
+    b, VeRA e, and the shared B_sh once; decode_prologue (rotation, shrinks):
+    x, A', P, VeRA d, shared A_sh; generic gemm: x, W, y.
+    """
     es = 2 if wl.dtype == "bf16" else 4
     xwy = wl.n * wl.d_in * es + wl.d_in * wl.d_out * es + wl.n * wl.d_out * 4
-    if name in ("forward", "fused"):
-        return cost["bytes"]
+    if name == "decode_main":
+        return cost["gemm_bytes"]
+    if name == "decode_prologue":
+        return cost["prologue_bytes"]
     if name == "gemm":
         return xwy
     return None

@@ -112,6 +112,9 @@ typedef struct scute_cost {
   int32_t n_rot_rows;   /* rows with a rotation slot (OFT)                   */
   int32_t n_vera_rows;  /* rows with a shared VeRA term                      */
   int32_t n_touched;    /* distinct adapters with at least one token         */
+  /* the same bytes split by the step that needs them (x counted in both):  */
+  double gemm_bytes;     /* base GEMM + expand: x, W, y, B', s, b, VeRA e, B_sh */
+  double prologue_bytes; /* rotation + shrink: x, A', P, VeRA d, A_sh          */
 } scute_cost;
 
 /* Create a layer context for one (d_in, d_out, activation dtype, device).
@@ -234,6 +237,7 @@ typedef struct scute_batch_info {
   int32_t n_rot_rows;  /* rows 0 .. n_rot_rows-1 of the sorted order rotate */
   int32_t n_vera_rows;
   int32_t max_rank;
+  int32_t path;        /* kernels the forward will run: 0 generic, 1 MFMA decode */
 } scute_batch_info;
 
 scute_status scute_batch_info_get(const scute_batch* batch, scute_batch_info* out);

@@ -229,41 +229,6 @@ __global__ void __launch_bounds__(256) k_expand_ref(const float* __restrict__ t,
 
 static inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
-// Kernel timing: when the layer has profiling on, bracket each launch with a
-// HIP event pair on the launch stream.
-struct ProfScope {
-  scute_layer* L;
-  hipStream_t st;
-  ProfEvent ev{};
-  bool on = false;
-  ProfScope(scute_layer* L_, hipStream_t st_, const char* name) : L(L_), st(st_) {
-    if (!L->profiling) return;
-    int32_t kind = -1;
-    for (size_t i = 0; i < L->prof_names.size(); ++i)
-      if (L->prof_names[i] == name) kind = (int32_t)i;
-    if (kind < 0) {
-      kind = (int32_t)L->prof_names.size();
-      L->prof_names.push_back(name);
-      L->prof_ms.push_back(0.0);
-      L->prof_count.push_back(0);
-    }
-    ev.kind = kind;
-    for (hipEvent_t* e : {&ev.start, &ev.stop}) {
-      if (!L->prof_pool.empty()) {
-        *e = L->prof_pool.back();
-        L->prof_pool.pop_back();
-      } else if (hipEventCreate(e) != hipSuccess) {
-        return;
-      }
-    }
-    on = hipEventRecord(ev.start, st) == hipSuccess;
-  }
-  ~ProfScope() {
-    if (!on) return;
-    if (hipEventRecord(ev.stop, st) == hipSuccess) L->prof_pending.push_back(ev);
-  }
-};
-
 template <typename T>
 static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x, const T* W,
                                float* y, hipStream_t st, int32_t* launches) {
@@ -311,12 +276,14 @@ static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x,
 int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
   (void)L;
   if (B->n == 0) return 0;
+  if (B->dp.enabled) return 1 + ((B->dp.S > 1 || B->dp.n_pro > 0) ? 1 : 0);
   return (B->n_rot > 0) + (B->max_rank > 0) + (B->n_vera > 0) + 1 +
          (B->max_rank > 0 || B->n_vera > 0);
 }
 
 scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                             float* y, hipStream_t st, int32_t* launches) {
+  if (B->dp.enabled) return launch_decode(L, B, x, W, y, st, launches);
   if (L->act == SCUTE_BF16)
     return launch_ref<uint16_t>(L, B, (const uint16_t*)x, (const uint16_t*)W, y, st, launches);
   return launch_ref<float>(L, B, (const float*)x, (const float*)W, y, st, launches);

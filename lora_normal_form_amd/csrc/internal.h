@@ -76,6 +76,37 @@ struct scute_layer {
   std::vector<int32_t> prof_count;
 };
 
+namespace scute {
+
+// Tables and workspaces of the MFMA decode path (bf16, small batches).
+struct DecodePlan {
+  bool enabled = false;
+  int32_t MG = 0;       // row groups of 32 covering the n sorted rows
+  int32_t g_rot = 0;    // leading row groups that hold rotated rows
+  int32_t M_pad = 0;    // 32 * MG
+  int32_t RT = 0;       // row stride of tb (max own rank rounded up to 16)
+  int32_t S = 1;        // K splits of the base GEMM
+  int32_t C = 0;        // column tiles of 128 outputs
+  int32_t k_chunk = 0;  // d_in / S
+  int32_t n_pro = 0;    // prologue work items
+  int32_t nvb = 0, njb = 0, SV = 0, KV = 0;  // VeRA shrink blocking
+  const int32_t* row_tok = nullptr;  // [M_pad] token index, -1 past n
+  const float* const* row_s = nullptr;   // [M_pad] live s of the row's adapter or null
+  const float* const* row_b = nullptr;   // [M_pad] shift b or null
+  const float* const* row_ve = nullptr;  // [M_pad] VeRA e or null
+  const int4* pro_items = nullptr;   // [n_pro]
+  const int4* exp_items = nullptr;   // expand items grouped by K split
+  const int32_t* exp_off = nullptr;  // [S + 1]
+  uint16_t* tb = nullptr;     // [M_pad][RT] bf16 own-term shrink
+  uint16_t* ub = nullptr;     // [M_pad][r_v] bf16 VeRA shrink (times d)
+  uint16_t* delta = nullptr;  // [32 * g_rot][d_in] bf16 x (R - I)
+  float* vpart = nullptr;     // [SV][nvb * njb][1024] VeRA shrink partials
+  int32_t* vcnt = nullptr;    // [nvb * njb] arrival counters (kept at zero)
+  int32_t n_exp = 0;
+};
+
+}  // namespace scute
+
 struct scute_batch {
   const scute_layer* layer = nullptr;
   uint64_t epoch = 0;
@@ -99,6 +130,8 @@ struct scute_batch {
   void* delta = nullptr;      // [n_rot][d_in] act dtype: x (R - I)
   float* t = nullptr;         // [n][max_rank]  own-term shrink
   float* u = nullptr;         // [n][r_v] VeRA shrink scaled by d (rows with VeRA)
+  void* fast_dev = nullptr;   // decode-path tables + workspaces (one allocation)
+  scute::DecodePlan dp;
   int32_t nseg() const { return (int32_t)(seg.size() / 3); }
 };
 
@@ -120,5 +153,45 @@ scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x,
                             const void* W, float* y, hipStream_t stream,
                             int32_t* launches_out);
 int32_t forward_launch_count(const scute_layer* L, const scute_batch* B);
+
+// decode path (decode.hip / plan.cpp)
+scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t st);
+scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, const void* W,
+                           float* y, hipStream_t st, int32_t* launches);
+
+// Kernel timing: when the layer has profiling on, bracket each launch with a
+// HIP event pair on the launch stream.
+struct ProfScope {
+  scute_layer* L;
+  hipStream_t st;
+  ProfEvent ev{};
+  bool on = false;
+  ProfScope(scute_layer* L_, hipStream_t st_, const char* name) : L(L_), st(st_) {
+    if (!L->profiling) return;
+    int32_t kind = -1;
+    for (size_t i = 0; i < L->prof_names.size(); ++i)
+      if (L->prof_names[i] == name) kind = (int32_t)i;
+    if (kind < 0) {
+      kind = (int32_t)L->prof_names.size();
+      L->prof_names.push_back(name);
+      L->prof_ms.push_back(0.0);
+      L->prof_count.push_back(0);
+    }
+    ev.kind = kind;
+    for (hipEvent_t* e : {&ev.start, &ev.stop}) {
+      if (!L->prof_pool.empty()) {
+        *e = L->prof_pool.back();
+        L->prof_pool.pop_back();
+      } else if (hipEventCreate(e) != hipSuccess) {
+        return;
+      }
+    }
+    on = hipEventRecord(ev.start, st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    if (hipEventRecord(ev.stop, st) == hipSuccess) L->prof_pending.push_back(ev);
+  }
+};
 
 }  // namespace scute

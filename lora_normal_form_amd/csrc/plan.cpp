@@ -39,9 +39,10 @@ void free_batch_memory(scute_batch* B) {
     if (prev != dev) (void)hipSetDevice(dev);
     if (B->dev) (void)hipFree(B->dev);
     if (B->ws) (void)hipFree(B->ws);
+    if (B->fast_dev) (void)hipFree(B->fast_dev);
     if (prev != dev && prev >= 0) (void)hipSetDevice(prev);
   }
-  B->dev = B->ws = nullptr;
+  B->dev = B->ws = B->fast_dev = nullptr;
 }
 
 }  // namespace
@@ -145,11 +146,18 @@ extern "C" scute_status scute_plan_batch(scute_layer* L, const int32_t* token_ad
           B->u = B->n_vera ? (float*)(w + w_delta + w_t) : nullptr;
         }
       }
-      restore();
       if (e != hipSuccess) {
+        restore();
         free_batch_memory(B);
         delete B;
         return hip_fail(e, "plan upload / workspace");
+      }
+      scute_status ds = build_decode_plan(L, B, s);
+      restore();
+      if (ds != SCUTE_OK) {
+        free_batch_memory(B);
+        delete B;
+        return ds;
       }
     }
     *out = B;
@@ -175,6 +183,7 @@ extern "C" scute_status scute_batch_info_get(const scute_batch* B, scute_batch_i
   out->n_rot_rows = B->n_rot;
   out->n_vera_rows = B->n_vera;
   out->max_rank = B->max_rank;
+  out->path = B->dp.enabled ? 1 : 0;
   return SCUTE_OK;
 }
 
@@ -193,7 +202,8 @@ extern "C" scute_status scute_cost_model(const scute_layer* L, const scute_batch
   memset(out, 0, sizeof(*out));
   const double es = (double)dtype_size(L->act);
   const double n = B->n, din = (double)L->d_in, dout = (double)L->d_out;
-  double adapter = 0.0, flops_extra = 0.0;
+  double adapter = 0.0, flops_extra = 0.0, gemm_side = 0.0, pro_side = 0.0;
+  bool any_pro = false;
   bool any_vera = false;
   std::vector<char> seen(L->max_adapters, 0);
   for (int32_t p = 0; p < B->n; ++p) {
@@ -204,7 +214,11 @@ extern "C" scute_status scute_cost_model(const scute_layer* L, const scute_batch
     if (!seen[a]) {
       seen[a] = 1;
       for (int i = 0; i < 7; ++i) adapter += (double)S.len[i];
+      gemm_side += (double)(S.len[SCUTE_SLOT_B] + S.len[SCUTE_SLOT_S] + S.len[SCUTE_SLOT_BIAS] +
+                            S.len[SCUTE_SLOT_VE]);
+      pro_side += (double)(S.len[SCUTE_SLOT_A] + S.len[SCUTE_SLOT_VD] + S.len[SCUTE_SLOT_P]);
     }
+    if (E.flags & (F_TERM | F_VERA | F_R)) any_pro = true;
     if (E.flags & F_TERM) flops_extra += 2.0 * (din * E.rank + E.rank * dout);
     if (E.flags & F_VERA) {
       any_vera = true;
@@ -214,6 +228,11 @@ extern "C" scute_status scute_cost_model(const scute_layer* L, const scute_batch
   }
   if (any_vera) adapter += (double)L->r_v * (din + dout) * es;
   const double xwy = n * din * es + din * dout * es + n * dout * 4.0;
+  if (B->n) {
+    out->gemm_bytes = xwy + gemm_side + (any_vera ? (double)L->r_v * dout * es : 0.0);
+    out->prologue_bytes =
+        any_pro ? n * din * es + pro_side + (any_vera ? (double)L->r_v * din * es : 0.0) : 0.0;
+  }
   out->bytes = (B->n ? xwy : 0.0) + adapter;
   out->adapter_bytes = adapter;
   out->base_flops = 2.0 * n * din * dout;

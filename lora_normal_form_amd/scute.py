@@ -49,7 +49,8 @@ class Cost(C.Structure):
     _fields_ = [("bytes", C.c_double), ("adapter_bytes", C.c_double), ("flops", C.c_double),
                 ("base_flops", C.c_double), ("launches", C.c_int32), ("n_tokens", C.c_int32),
                 ("n_segments", C.c_int32), ("n_rot_rows", C.c_int32),
-                ("n_vera_rows", C.c_int32), ("n_touched", C.c_int32)]
+                ("n_vera_rows", C.c_int32), ("n_touched", C.c_int32),
+                ("gemm_bytes", C.c_double), ("prologue_bytes", C.c_double)]
 
 
 class AdapterInfo(C.Structure):
@@ -60,7 +61,7 @@ class AdapterInfo(C.Structure):
 
 class BatchInfo(C.Structure):
     _fields_ = [("n", C.c_int32), ("n_segments", C.c_int32), ("n_rot_rows", C.c_int32),
-                ("n_vera_rows", C.c_int32), ("max_rank", C.c_int32)]
+                ("n_vera_rows", C.c_int32), ("max_rank", C.c_int32), ("path", C.c_int32)]
 
 
 class KernelTime(C.Structure):

@@ -121,12 +121,27 @@ def test_far_from_identity_vectors():
     _assert_parity(wl, y)
 
 
-def test_repeat_runs_identical_and_plan_reuse():
+def test_repeat_runs_and_plan_reuse():
+    # the MFMA decode path adds K-slice partials with float atomics, so
+    # repeated runs agree to rounding, not bit for bit; the generic kernels
+    # are deterministic
     _need_gpu()
     wl, ref = _config(2)
     ld, y1 = _run(wl)
     _, y2 = _run(wl, loaded=ld)
-    np.testing.assert_array_equal(y1, y2)
+    assert np.max(np.abs(y1 - y2)) <= 1e-5 * np.max(np.abs(ref))
+    import os
+    from lora_normal_form_amd import workload as glue
+    os.environ["SCUTE_DECODE"] = "0"
+    try:
+        ldg = glue.load(wl, device=0)
+    finally:
+        del os.environ["SCUTE_DECODE"]
+    assert ldg.batch.info()["path"] == 0
+    _, g1 = _run(wl, loaded=ldg)
+    _, g2 = _run(wl, loaded=ldg)
+    np.testing.assert_array_equal(g1, g2)
+    _assert_parity(wl, g1, ref)
     # same plan, new activations
     from lora_normal_form_amd import workload as glue
     rng = np.random.default_rng(8)
