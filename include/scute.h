@@ -211,7 +211,9 @@ typedef enum scute_slot {
   SCUTE_SLOT_BIAS = 3, /* b [d_out]                   float32          */
   SCUTE_SLOT_VD = 4, /* VeRA d [r_v]                  float32          */
   SCUTE_SLOT_VE = 5, /* VeRA e, c folded [d_out]      float32          */
-  SCUTE_SLOT_P = 6   /* R - I [d_in/blk][blk][blk]    activation dtype */
+  SCUTE_SLOT_P = 6   /* R - I [d_in/blk][blk][blk]    activation dtype
+                        (kept transposed per block on the device;
+                        scute_read_slot returns R - I itself)         */
 } scute_slot;
 
 typedef struct scute_adapter_info {

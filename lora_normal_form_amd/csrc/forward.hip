@@ -36,7 +36,8 @@ __device__ __forceinline__ void stf(uint16_t* p, size_t i, float v) {
 }
 
 // ---------------------------------------------------------------------------
-// rotation: delta[p][col] = sum_i x[perm[p]][kb*blk + i] * P[kb][i][col - kb*blk]
+// rotation: delta[p][col] = sum_i x[perm[p]][kb*blk + i] * P[kb][i][col - kb*blk],
+// P stored transposed per block
 // grid (ceil(d_in / 256), n_rot)
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -52,9 +53,9 @@ __global__ void __launch_bounds__(256) k_rotate_ref(const T* __restrict__ x,
   const int32_t blk = E.blk;
   const int64_t kb = col / blk, jj = col - kb * blk;
   const T* xr = x + (size_t)perm[p] * d_in + kb * blk;
-  const T* P = (const T*)E.P + (size_t)kb * blk * blk;
+  const T* Pt = (const T*)E.P + ((size_t)kb * blk + jj) * blk;  // (R - I)^T row jj
   float acc = 0.f;
-  for (int32_t i = 0; i < blk; ++i) acc += ldf(xr, i) * ldf(P, (size_t)i * blk + jj);
+  for (int32_t i = 0; i < blk; ++i) acc += ldf(xr, i) * ldf(Pt, i);
   stf(delta, (size_t)p * d_in + col, acc);
 }
 

@@ -86,23 +86,31 @@ struct DecodePlan {
   int32_t M_pad = 0;    // 32 * MG
   int32_t RT = 0;       // row stride of tb (max own rank rounded up to 16)
   int32_t S = 1;        // K splits of the base GEMM
-  int32_t C = 0;        // column tiles of 128 outputs
+  int32_t C = 0;        // column tiles of 64 outputs
   int32_t k_chunk = 0;  // d_in / S
   int32_t n_pro = 0;    // prologue work items
-  int32_t nvb = 0, njb = 0, SV = 0, KV = 0;  // VeRA shrink blocking
+  int32_t nvb = 0, njb = 0, SV = 0;  // VeRA shrink blocking (K slices of 512)
   const int32_t* row_tok = nullptr;  // [M_pad] token index, -1 past n
-  const float* const* row_s = nullptr;   // [M_pad] live s of the row's adapter or null
-  const float* const* row_b = nullptr;   // [M_pad] shift b or null
-  const float* const* row_ve = nullptr;  // [M_pad] VeRA e or null
+  const float* const* row_s = nullptr;   // [256] live s of the row's adapter or null
+  const float* const* row_b = nullptr;   // [256] shift b or null
+  const float* const* row_ve = nullptr;  // [256] VeRA e or null
   const int4* pro_items = nullptr;   // [n_pro]
   const int4* exp_items = nullptr;   // expand items grouped by K split
+  const uint16_t* const* exp_ptr = nullptr;  // per expand item: B' or B_sh
   const int32_t* exp_off = nullptr;  // [S + 1]
+  const float* ones = nullptr;  // [d_out] of 1.0f
   uint16_t* tb = nullptr;     // [M_pad][RT] bf16 own-term shrink
   uint16_t* ub = nullptr;     // [M_pad][r_v] bf16 VeRA shrink (times d)
   uint16_t* delta = nullptr;  // [32 * g_rot][d_in] bf16 x (R - I)
   float* vpart = nullptr;     // [SV][nvb * njb][1024] VeRA shrink partials
   int32_t* vcnt = nullptr;    // [nvb * njb] arrival counters (kept at zero)
   int32_t n_exp = 0;
+  const int4* sgroups = nullptr;  // own-term shrink groups
+  float* spart = nullptr;     // [KQ][n_sgroups][16] shrink partials
+  int32_t* scnt = nullptr;    // [n_sgroups] shrink arrival counters
+  int32_t n_sgroups = 0, KQ = 0;
+  float* part = nullptr;      // [S][C][2][MG][16][64] split-K partials (S > 1)
+  int32_t* cnt = nullptr;     // [C] arrival counters (kept at zero)
 };
 
 }  // namespace scute

@@ -431,9 +431,11 @@ scute_status fold_adapter(const scute_layer* L, const scute_adapter_desc* D, con
       } else {
         for (int32_t i = 0; i < blk * blk; ++i) X[i] = load_elem(D->R, dt, base + i);
       }
+      // stored transposed, (R - I)^T: element [kb][j][i] = (R - I)[kb][i][j],
+      // so one output column's block entries are contiguous
       for (int32_t i = 0; i < blk; ++i)
         for (int32_t j = 0; j < blk; ++j)
-          store_act(F.P.data(), act, base + (size_t)i * blk + j,
+          store_act(F.P.data(), act, base + (size_t)j * blk + i,
                     X[(size_t)i * blk + j] - ((i == j) ? 1.0 : 0.0));
     }
     F.flags |= F_R;
@@ -582,6 +584,19 @@ extern "C" scute_status scute_read_slot(const scute_layer* L, int32_t id, int32_
     SCUTE_HIP_CHECK(hipMemcpy(dst, src, S.len[slot], hipMemcpyDeviceToHost));
   } else {
     memcpy(dst, src, S.len[slot]);
+  }
+  if (slot == SCUTE_SLOT_P) {
+    // storage holds (R - I)^T per block; hand back R - I
+    const int32_t blk = L->table[id].blk;
+    const size_t es = dtype_size(L->act), nb = (size_t)L->d_in / blk;
+    std::vector<uint8_t> blkbuf((size_t)blk * blk * es);
+    for (size_t kb = 0; kb < nb; ++kb) {
+      uint8_t* b = (uint8_t*)dst + kb * blk * blk * es;
+      memcpy(blkbuf.data(), b, blkbuf.size());
+      for (int32_t i = 0; i < blk; ++i)
+        for (int32_t j = 0; j < blk; ++j)
+          memcpy(b + ((size_t)i * blk + j) * es, blkbuf.data() + ((size_t)j * blk + i) * es, es);
+    }
   }
   return SCUTE_OK;
 }

@@ -60,6 +60,11 @@ def _check(wl, y, ref=None):
     assert np.all(np.isfinite(y))
     ok, rep = oracle.check(y, ref, wl.x @ wl.W.T, wl.token_adapter, wl.dtype)
     print(f"[gpu] {rep}", flush=True)
+    if not ok:
+        eff = oracle.effect_errors(y, ref, wl.x @ wl.W.T, wl.token_adapter)
+        meth = {a.id: a.method for a in wl.adapters}
+        bad = {f"{aid}:{meth[aid]}": round(e, 4) for aid, e in eff.items() if e > 0.01}
+        print(f"[gpu] adapters over 1%: {bad}", flush=True)
     assert ok, rep
     return ref
 
@@ -85,8 +90,20 @@ def _wl(n, seed, d_in=512, d_out=384, vera_rank=64, none_frac=0.1, adapters=MIX,
 
 @pytest.mark.parametrize("n", [1, 5, 33, 77, 128, 200, 256])
 def test_decode_path_mixed(n):
+    # the MFMA path stages ceil(n / 32) row groups plus one per 32 rotated
+    # rows, at most 9; larger batches run the generic kernels
     _need_gpu()
     wl = _wl(n, seed=n)
+    ld, y = _forward(wl)
+    info = ld.batch.info()
+    groups = -(-n // 32) + -(-info["n_rot_rows"] // 32)
+    assert info["path"] == (1 if groups <= 9 else 0), info
+    _check(wl, y)
+
+
+def test_decode_path_256_rows_few_rotated():
+    _need_gpu()
+    wl = _wl(256, seed=21, adapters=MIX[:4] + MIX[5:7] + MIX[8:9] + MIX[10:])
     _, y = _forward(wl, expect_path=1)
     _check(wl, y)
 
