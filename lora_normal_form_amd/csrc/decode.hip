@@ -1,28 +1,37 @@
 // MFMA decode path (bf16 activations, fp32 accumulate, up to 256 rows).
 //
-// Two kernels per forward:
-//   k_decode_prologue: zero y (when the GEMM splits K), OFT rotation
-//     delta = x (R - I), own-term shrink t = x A', VeRA shrink over the whole
-//     batch u = (x A_sh) (.) d. Rotation runs before the shared GEMM and the
-//     shared VeRA pair is read once per step ("Where is the cheapest place to
-//     compute the remaining slots?", paper-daily.com explainer of "Scute:
-//     Exact Batched Serving for PEFT Adapters Beyond LoRA").
-//   k_decode_main: the shared GEMM y = (x W + delta W) (.) s + b for the whole
-//     batch on 32x32x16 bf16 MFMA, then the expand in the epilogue: the own
-//     low-rank update t B' and the VeRA term (u B_sh) (.) e, added unscaled
-//     by s ("The big picture": s multiplies the base output, the low-rank sum
-//     is added after).
+// Two kernels per forward.
 //
-// Layout of the main kernel. A work-group of 4 waves owns 128 output columns
-// (32 per wave) and one of S slices of the K dimension; its partial product
-// for all rows (row groups of 32) is scaled by s and added into y with float
-// atomics (y zeroed by the prologue) when S > 1, stored directly when S = 1.
-// W is the MFMA B operand, streamed from HBM straight into registers: each
-// lane loads 64 contiguous bytes of one W row per 128-wide K block (two 32-k
-// halves of a 64-k sub-block); the MFMA's k index is permuted consistently on
-// both operands so the contraction is unchanged. x (and delta) rows are the
-// A operand, staged in LDS with direct global->LDS loads, 256-byte rows with
-// the 16-byte chunk index XOR-swizzled by the row to spread LDS banks.
+// k_decode_prologue works on small items, one per wave:
+//   rotation    delta = x (R - I) for up to 4 rotated rows and 64 columns
+//               (R is block-diagonal, so a column needs one block of x);
+//   own shrink  t = x A' for up to 4 rows x 4 ranks over a K part of 1024;
+//   VeRA shrink u = (x A_sh) (.) d for 32 VeRA rows x 32 ranks over a K
+//               slice of 512, on one 32x32x16 MFMA tile.
+// Rotation runs before the shared GEMM and the shared VeRA pair is read once
+// per step for the whole batch ("Where is the cheapest place to compute the
+// remaining slots?", paper-daily.com explainer of "Scute: Exact Batched
+// Serving for PEFT Adapters Beyond LoRA"). The K parts of a shrink meet
+// through a small workspace: every part stores its partial sums and the last
+// part to arrive adds them all in K order (so the result does not depend on
+// arrival order) and writes the bf16 result.
+//
+// k_decode_main computes, per work-group of 4 waves, 64 output columns over
+// one of S slices of K for all rows of the batch:
+//   base     x W and delta W on 32x32x16 bf16 MFMA: x / delta rows staged in
+//            LDS by direct global->LDS loads through a ring of 64-k stages,
+//            W streamed straight into registers;
+//   epilogue the accumulators move to an LDS tile. Row-wise passes (16
+//            threads per row, so each row's factor vectors are read through
+//            a row-uniform pointer with coalesced 16-byte accesses) fold
+//            delta W into the rotated rows and scale by s; the expand adds
+//            the own low-rank product t B' (not scaled by s: "The big
+//            picture", s multiplies the base output only) and forms the
+//            VeRA product u B_sh, which the last pass scales by e and adds
+//            with b.
+// With S > 1 the slices of a tile meet through a workspace written and read
+// with system-coherent accesses; the last slice to arrive adds the slices in
+// slice order and writes y.
 
 #include <algorithm>
 
@@ -32,7 +41,10 @@ namespace scute {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 namespace {
 
@@ -41,9 +53,6 @@ __device__ __forceinline__ uint16_t f2bf(float v) {
   uint32_t u = __float_as_uint(v);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
 __device__ __forceinline__ bf16x8 as_frag(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
@@ -57,15 +66,12 @@ template <typename T>
 __device__ __forceinline__ T ldg(const T* p) {
   return *(const GLOBAL T*)p;
 }
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
   const u32x4 v = *(const GLOBAL u32x4*)p;
   return make_uint4(v.x, v.y, v.z, v.w);
 }
-__device__ __forceinline__ uint4 ldg16_stream(const uint16_t* p) {
-  const u32x4 v = __builtin_nontemporal_load((const GLOBAL u32x4*)p);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
+__device__ __forceinline__ f32x4 ldg4(const float* p) { return *(const GLOBAL f32x4*)p; }
+__device__ __forceinline__ void stg4(float* p, f32x4 v) { *(GLOBAL f32x4*)p = v; }
 __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
   float s = 0.f;
@@ -76,19 +82,42 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   }
   return s;
 }
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Raw buffer resources over a byte range: loads past the range return zero,
+// stores past it are dropped. (The third word's data-format field must be
+// non-zero on gfx9 for raw dword accesses.)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ldb16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Exchange of partial results between work-groups on any XCD without
 // whole-cache maintenance: the exchanged values are written and read with
-// system-scope relaxed atomic stores and loads (sc0 sc1: written through to
-// memory and read from memory, past the per-XCD L2). Being ordinary
-// compiler-visible memory operations, their results are waited for by the
-// compiler. A writer waits for its stores to complete before announcing them
+// system-coherent buffer accesses (cache policy sc0 sc1: written through to
+// memory, read from memory, past the per-XCD L2). They are ordinary
+// compiler-visible memory operations, so the compiler waits for their
+// results. A writer waits for its stores to complete before announcing them
 // with an atomic on a counter; a reader issues its loads only after the
 // atomic that saw every announcement has returned.
-__device__ __forceinline__ void st_coh(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+constexpr int CPOL_SYS = 17;  // sc0 | sc1
+__device__ __forceinline__ void st_sys(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CPOL_SYS);
 }
-__device__ __forceinline__ float ld_coh(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+__device__ __forceinline__ float ld_sys(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_SYS));
+}
+__device__ __forceinline__ void st_sys4(rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL_SYS);
+}
+__device__ __forceinline__ f32x4 ld_sys4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_SYS));
 }
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int arrive(int32_t* cnt) {
@@ -96,11 +125,6 @@ __device__ __forceinline__ int arrive(int32_t* cnt) {
 }
 __device__ __forceinline__ void reset_counter(int32_t* cnt) {
   __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
 }
 
 enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2 };
@@ -114,88 +138,73 @@ enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
 
 struct ProArgs {
   const uint16_t* x;
-  const int32_t* perm;         // sorted position -> token
-  const int32_t* row_adapter;  // sorted position -> adapter
-  const int32_t* vera_pos;     // VeRA row index -> sorted position
-  const SlotEntry* table;
-  const uint16_t* A_sh;        // [r_v][d_in]
-  float* y;                    // zeroed when zero_y
-  int64_t y_vec4;              // n * d_out / 4
-  int32_t zero_y;
-  const int4* items;
+  const DecProItem* items;
   int32_t n_items;
-  uint16_t* tb;                // [M_pad][RT]
+  const DecVeraRow* vrows;  // [32 nvb]
+  const uint16_t* A_sh;     // [r_v][d_in]
+  uint16_t* tb;             // [M_pad][RT]
   int32_t RT;
-  uint16_t* ub;                // [M_pad][r_v]
+  uint16_t* ub;             // [M_pad][r_v]
   int32_t r_v;
-  uint16_t* delta;             // [32 g_rot][d_in]
-  float* vpart;                // [SV][nvb * njb][1024]
-  int32_t* vcnt;               // [nvb * njb]
-  int32_t nvb, njb, SV, n_vera;
-  int32_t d_in;
-  const int4* sgroups;         // own-term shrink groups (first row, rows, first rank, ranks)
-  float* spart;                // [KQ][n_sgroups][16] partial dot products
-  int32_t* scnt;               // [n_sgroups] arrival counters (kept at zero)
+  uint16_t* delta;          // [32 g_rot][d_in]
+  float* spart;             // [KQ][n_sgroups][16]
+  int32_t* scnt;            // [n_sgroups]
+  uint32_t spart_bytes;
   int32_t n_sgroups, KQ;
+  float* vpart;             // [SV][nvb * njb][16][64]
+  int32_t* vcnt;            // [nvb * njb]
+  uint32_t vpart_bytes;
+  int32_t nvb, njb, SV;
+  int32_t d_in;
 };
 
-// delta rows for one rotated segment chunk (<= R rows, one 64-column chunk):
-// lane handles output column col = c0 + lane of block kb = col / blk; the
-// block's (R - I)^T row for that column and the rows' x block are contiguous,
-// read in CH-wide vector batches (blk a multiple of CH)
-template <int CH, int R>
-__device__ __forceinline__ void rotate_rows(const ProArgs& a, const uint16_t* Pt, int32_t blk,
-                                            const uint16_t* const (&xr)[R], int32_t nr,
-                                            int64_t col, float (&acc)[R]) {
+// delta rows for one rotated item (<= 4 rows, one 64-column chunk): lane
+// handles output column col of block kb = col / blk; the block's (R - I)^T
+// row for that column and the rows' x block are contiguous, read in CH-wide
+// vector batches (blk a multiple of CH)
+template <int CH>
+__device__ __forceinline__ void rotate_rows(const uint16_t* Pt, int32_t blk,
+                                            const uint16_t* const (&xr)[4], int64_t col,
+                                            float (&acc)[4]) {
   const int64_t kb = col / blk, jj = col - kb * blk;
   const uint16_t* prow = Pt + ((size_t)kb * blk + jj) * blk;
   for (int32_t i0 = 0; i0 < blk; i0 += CH) {
-    uint4 pv[CH / 8], xv[R][CH / 8];
+    uint4 pv[CH / 8], xv[4][CH / 8];
 #pragma unroll
     for (int q = 0; q < CH / 8; ++q) pv[q] = ldg16(prow + i0 + 8 * q);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < CH / 8; ++q) xv[r][q] = ldg16(xr[r] + kb * blk + i0 + 8 * q);
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int q = 0; q < CH / 8; ++q) acc[r] += dot8(xv[r][q], pv[q]);
   }
-  (void)nr;
 }
 
 __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
   const int lane = threadIdx.x & 63;
-  if (a.zero_y) {
-    float4* y4 = reinterpret_cast<float4*>(a.y);
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < a.y_vec4;
-         i += (int64_t)gridDim.x * 256)
-      y4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int64_t d_in = a.d_in;
-  for (int it = blockIdx.x * 4 + (threadIdx.x >> 6); it < a.n_items; it += gridDim.x * 4) {
-    const int4 item = a.items[it];
-    if (item.x == PRO_ROT) {
-      // delta[p][col] = sum_i x[tok p][kb*blk + i] (R - I)[kb][i][col - kb*blk]
-      // item: (first sorted row, rows <= 4, first of 64 columns)
-      const int32_t p0 = item.y, len = item.z;
-      const int64_t col = (int64_t)item.w + lane;
-      const SlotEntry E = a.table[a.row_adapter[p0]];
-      const int32_t blk = E.blk;
-      const uint16_t* Pt = (const uint16_t*)E.P;
+  for (int it = blockIdx.x * 4 + wave; it < a.n_items; it += gridDim.x * 4) {
+    const DecProItem item = a.items[it];
+    if (item.type == PRO_ROT) {
+      // delta[p][col] = sum_i x[tok p][kb blk + i] (R - I)[kb][i][col - kb blk]
+      const int64_t col = (int64_t)item.k + lane;
+      const int32_t blk = item.blk;
       const uint16_t* xr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xr[r] = a.x + (size_t)a.perm[p0 + min(r, len - 1)] * d_in;
+      for (int r = 0; r < 4; ++r) xr[r] = a.x + (size_t)item.tok[r] * d_in;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
       if (col < d_in) {
         if (blk % 32 == 0) {
-          rotate_rows<32, 4>(a, Pt, blk, xr, len, col, acc);
+          rotate_rows<32>(item.ptr, blk, xr, col, acc);
         } else if (blk % 8 == 0) {
-          rotate_rows<8, 4>(a, Pt, blk, xr, len, col, acc);
+          rotate_rows<8>(item.ptr, blk, xr, col, acc);
         } else {
           const int64_t kb = col / blk, jj = col - kb * blk;
-          const uint16_t* prow = Pt + ((size_t)kb * blk + jj) * blk;
+          const uint16_t* prow = item.ptr + ((size_t)kb * blk + jj) * blk;
           for (int32_t i = 0; i < blk; ++i) {
             const float pv = bf2f(ldg(prow + i));
 #pragma unroll
@@ -204,25 +213,20 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (r < len) a.delta[(size_t)(p0 + r) * d_in + col] = f2bf(acc[r]);
+          if (r < item.n) a.delta[(size_t)(item.p0 + r) * d_in + col] = f2bf(acc[r]);
       }
-    } else if (item.x == PRO_SHRINK) {
+    } else if (item.type == PRO_SHRINK) {
       // own-term shrink t = x A' for up to 4 rows x 4 ranks over one K part
-      // of 1024; the K parts meet through a small partial buffer, the last
-      // to arrive sums them in K order and writes tb (bf16).
-      // item: (group index, first row | rows << 16, first rank | ranks << 16 ...)
-      const int32_t grp = item.y;
-      const int4 gd = a.sgroups[grp];  // (first row, rows, first rank, ranks)
-      const int32_t p0 = gd.x, len = gd.y, k0 = gd.z, nk = gd.w, kq = item.z;
-      const SlotEntry E = a.table[a.row_adapter[p0]];
-      const uint16_t* A = (const uint16_t*)E.A;
+      // of 1024; the last K part to arrive sums the parts in K order
+      const int32_t len = item.n, k0 = item.k & 0xFFFF, nk = item.k >> 16;
+      const int32_t kq = item.blk, grp = item.grp;
       const int64_t cbeg = (int64_t)kq * 1024;
       const uint16_t* ar[4];
       const uint16_t* xr[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ar[j] = A + (size_t)(k0 + min(j, nk - 1)) * d_in + cbeg;
+      for (int j = 0; j < 4; ++j) ar[j] = item.ptr + (size_t)(k0 + min(j, nk - 1)) * d_in + cbeg;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xr[r] = a.x + (size_t)a.perm[p0 + min(r, len - 1)] * d_in + cbeg;
+      for (int r = 0; r < 4; ++r) xr[r] = a.x + (size_t)item.tok[r] * d_in + cbeg;
       float acc[4][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -246,7 +250,6 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[r][j] += dot8(xv[cc][r], av[cc][j]);
       }
-      float* part = a.spart + ((size_t)kq * a.n_sgroups + grp) * 16;
       float mine = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -255,31 +258,44 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
           const float v = wave_sum(acc[r][j]);
           if (lane == 4 * r + j) mine = v;
         }
-      if (lane < 16) st_coh(part + lane, mine);
+      const rsrc_t pr = make_rsrc(a.spart, a.spart_bytes);
+      if (lane < 16) st_sys(pr, (uint32_t)(((kq * a.n_sgroups + grp) * 16 + lane) * 4), mine);
       wait_vm_all();
       int32_t old = 0;
       if (lane == 0) old = arrive(&a.scnt[grp]);
       old = __shfl(old, 0, 64);
       if (old == a.KQ - 1) {
-        if (lane < 16) {
-          float tot = 0.f;
-          for (int32_t q = 0; q < a.KQ; ++q)
-            tot += q == kq ? mine : ld_coh(a.spart + ((size_t)q * a.n_sgroups + grp) * 16 + lane);
-          const int r = lane >> 2, j = lane & 3;
-          if (r < len && j < nk) a.tb[(size_t)(p0 + r) * a.RT + k0 + j] = f2bf(tot);
-        }
+        // parts past KQ lie past the workspace and read as zero
+        const int l16 = lane & 15;
+        float tot = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          tot += ld_sys(pr, (uint32_t)(((q * a.n_sgroups + grp) * 16 + l16) * 4));
+        const int r = l16 >> 2, j = l16 & 3;
+        if (lane < 16 && r < len && j < nk)
+          a.tb[(size_t)(item.p0 + r) * a.RT + k0 + j] = f2bf(tot);
         if (lane == 0) reset_counter(&a.scnt[grp]);
       }
     } else {
-      // VeRA shrink block: 32 VeRA rows x 32 rows of A_sh over one K slice of
-      // 512 (two rounds of loads), partial sums combined by the last of the
-      // SV slices to arrive
-      const int32_t vb = item.y, jb = item.z, kv = item.w;
+      // VeRA shrink block: 32 VeRA rows x 32 ranks of A_sh over one K slice
+      // of 512 (two rounds of loads); each slice scales its partial by d
+      // (d is per rank, so it commutes with the K sum) and the last of the
+      // SV slices to arrive adds them in slice order
+      const int32_t vb = item.p0, jb = item.n, kv = item.k;
       const int m = lane & 31, h = lane >> 5;
-      const int32_t vr = 32 * vb + m;
-      const int32_t vp = vr < a.n_vera ? a.vera_pos[vr] : a.vera_pos[0];
-      const uint16_t* xr = a.x + (size_t)a.perm[vp] * d_in + (int64_t)kv * 512 + 32 * h;
+      const DecVeraRow vr = a.vrows[32 * vb + m];
+      const uint16_t* xr = a.x + (size_t)vr.tok * d_in + (int64_t)kv * 512 + 32 * h;
       const uint16_t* ar = a.A_sh + (size_t)(32 * jb + m) * d_in + (int64_t)kv * 512 + 32 * h;
+      // output element i: VeRA row 32 vb + 8 (i / 4) + 4 h + i % 4, rank 32 jb + m
+      const int32_t j = 32 * jb + m;
+      float dsc[16];
+      int32_t prow[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const DecVeraRow o = a.vrows[32 * vb + 8 * (i >> 2) + 4 * h + (i & 3)];
+        prow[i] = o.p;
+        dsc[i] = ldg(o.vd + j);
+      }
       f32x16 acc = {};
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -292,43 +308,35 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc = mfma32(xa[q], wa[q], acc);
       }
-      const int32_t blkid = vb * a.njb + jb;
-      float* part = a.vpart + ((size_t)kv * a.nvb * a.njb + blkid) * 1024;
+      const int32_t blkid = vb * a.njb + jb, nblk = a.nvb * a.njb;
+      const rsrc_t pr = make_rsrc(a.vpart, a.vpart_bytes);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) st_coh(part + 64 * i + lane, acc[i]);
+      for (int i = 0; i < 16; ++i)
+        st_sys(pr, (uint32_t)((((kv * nblk + blkid) * 16 + i) * 64 + lane) * 4), acc[i] * dsc[i]);
       wait_vm_all();
       int32_t old = 0;
       if (lane == 0) old = arrive(&a.vcnt[blkid]);
       old = __shfl(old, 0, 64);
       if (old == a.SV - 1) {
+        // slices past SV lie past the workspace and read as zero
         float tot[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) tot[i] = 0.f;
-#pragma unroll 1
-        for (int32_t q = 0; q < a.SV; ++q) {
-          if (q == kv) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) tot[i] += acc[i];
-            continue;
-          }
-          const float* pq = a.vpart + ((size_t)q * a.nvb * a.njb + blkid) * 1024 + lane;
-          float pv[16];
+        for (int q = 0; q < 8; ++q)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) pv[i] = ld_coh(pq + 64 * i);
+          for (int i = 0; i < 16; ++i)
+            tot[i] += ld_sys(pr, (uint32_t)((((q * nblk + blkid) * 16 + i) * 64 + lane) * 4));
+        if (a.SV > 8) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) tot[i] += pv[i];
+          for (int q = 8; q < 16; ++q)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              tot[i] += ld_sys(pr, (uint32_t)((((q * nblk + blkid) * 16 + i) * 64 + lane) * 4));
         }
-        // acc element i: VeRA row 8(i/4) + 4h + i%4, A_sh row 32 jb + m
-        const int32_t j = 32 * jb + m;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int32_t row = 32 * vb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (row < a.n_vera) {
-            const int32_t p = a.vera_pos[row];
-            const float* vd = a.table[a.row_adapter[p]].vd;
-            a.ub[(size_t)p * a.r_v + j] = f2bf(tot[i] * ldg(vd + j));
-          }
-        }
+        for (int i = 0; i < 16; ++i)
+          if (prow[i] >= 0) a.ub[(size_t)prow[i] * a.r_v + j] = f2bf(tot[i]);
         if (lane == 0) reset_counter(&a.vcnt[blkid]);
       }
     }
@@ -342,29 +350,26 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
 struct MainArgs {
   const uint16_t* x;
   const uint16_t* W;
-  const uint16_t* delta;     // [32 g_rot][d_in]
-  const int32_t* row_tok;    // [M_pad], -1 past n
-  const float* const* row_s; // [256] per sorted row: live s, VeRA e, shift b (or null)
-  const float* const* row_ve;
-  const float* const* row_b;
-  const int4* items;         // expand items grouped by K slice
+  const uint16_t* delta;            // [32 g_rot][d_in]
+  const int32_t* row_tok;           // [M_pad] token staged for the row, -1 past n
+  const DecRow* rows;               // [M_pad]
+  const int4* items;                // expand items by slice, own then VeRA
   const uint16_t* const* item_ptr;  // per item: B' of its adapter (own) or B_sh (VeRA)
-  const int32_t* item_off;   // [S + 1]
-  const uint16_t* tb;        // [M_pad][RT] own-term shrink (bf16)
-  const uint16_t* ub;        // [M_pad][r_v] VeRA shrink (bf16), zero rows elsewhere
-  const float* ones;         // [d_out] of 1.0 (factor of rows without s or VeRA e)
-  float* part;               // split-K partials [S][C][2][mgx][16][64] (S > 1)
-  int32_t* cnt;              // [C] arrival counters, kept at zero between forwards
+  const int32_t* item_off;          // [2 S + 1]
+  const uint16_t* tb;               // [M_pad][RT] own-term shrink (bf16)
+  const uint16_t* ub;               // [M_pad][r_v] VeRA shrink (bf16), zero rows elsewhere
+  const float* zeros;               // [d_out]
+  float* part;                      // [S][C][M_pad][64] split-K partial tiles (S > 1)
+  int32_t* cnt;                     // [C] arrival counters, kept at zero between forwards
   float* y;
-  int32_t n, g_rot, d_in, d_out, k_chunk, S, C, RT, r_v;
+  uint32_t tb_bytes, ub_bytes, part_bytes;
+  int32_t g_rot, d_in, d_out, k_chunk, S, C, RT, r_v;
 };
 
 // Tile of the main kernel: 64 output columns (two 32-column MFMA blocks) by
 // one of S slices of K; the 4 waves of a work-group are (column block cb,
 // K half kp). The x / delta rows of each K half stream through an LDS ring
-// of R stages of 64 k; W streams straight into registers. The S slices of a
-// tile meet through a small workspace: the last slice to arrive adds the
-// others' partial products in slice order and writes y once.
+// of R stages of 64 k; W streams straight into registers.
 constexpr int SK = 64;                 // k per stage
 constexpr int SROW = 2 * SK;           // bytes per staged row
 template <int MGT>
@@ -400,9 +405,18 @@ __device__ __forceinline__ void stage_rows(uint8_t* stage, const uint16_t* const
                                      (lds_void*)(stage + (cb + 2 * q) * 1024), 16, 0, 0);
 }
 
-__device__ __forceinline__ void load_w(uint4 (&wr)[4], const uint16_t* wrow, int64_t koff) {
+// W of one stage for this lane: 64 contiguous bytes of its W row, addressed
+// by a fixed per-lane buffer offset plus the stage's scalar offset (no
+// per-load address registers)
+struct WSrc {
+  rsrc_t r;
+  uint32_t voff;
+};
+__device__ __forceinline__ void load_w(uint4 (&wr)[4], const WSrc& ws, int64_t koff) {
+  const int soff = (int)(koff * 2);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) wr[s] = ldg16(wrow + koff + 8 * s);
+  for (int s = 0; s < 4; ++s)
+    wr[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ws.r, ws.voff + 16 * s, soff, 0));
 }
 
 // one stage: 4 MFMA k-steps of 16 over every staged row group
@@ -425,8 +439,8 @@ __device__ __forceinline__ void mma_stage(const uint8_t* stage, const uint4 (&wr
 
 // pipeline step t: issue W(t+R-1), wait for stage t, barrier, issue the rows
 // of stage t+R-1 into the slot stage t-1 used, multiply stage t
-template <int MGT, int J>
-__device__ __forceinline__ void kstep(int t, int nst, const uint16_t* wrow,
+template <int MGT>
+__device__ __forceinline__ void kstep(int t, int nst, const WSrc& wrow,
                                       const uint16_t* const (&src)[2 * MGT], uint8_t* cur,
                                       uint8_t* nxt, uint4 (&wc)[4], uint4 (&wn)[4],
                                       f32x16 (&acc)[MGT], int m, int h, int cb, int kp) {
@@ -439,29 +453,119 @@ __device__ __forceinline__ void kstep(int t, int nst, const uint16_t* wrow,
   mma_stage<MGT>(cur + kp * DecCfg<MGT>::STAGE, wc, acc, m, h);
 }
 
-// MGT = staged row groups = ceil(n / 32) x groups + g_rot delta groups
-template <int MGT>
+// The same step with the stage index T known at compile time: stages past
+// the last are not prefetched, and the wait counts exactly the loads issued
+// after stage T's rows (R = 3: the next stage's W and rows, issued by the
+// previous step; this step's W), so no load is repeated and every wait is
+// exact. Expands to the steps T .. NST-1.
+template <int MGT, int NST, int T>
+__device__ __forceinline__ void ksteps_static(const WSrc& wrow, const uint16_t* const (&src)[2 * MGT],
+                                              uint8_t* s0, uint8_t* s1, uint8_t* s2,
+                                              uint4 (&wb)[3][4], f32x16 (&acc)[MGT], int m, int h,
+                                              int cb, int kp) {
+  if constexpr (T < NST) {
+    using Cfg = DecCfg<MGT>;
+    constexpr int R = Cfg::R;
+    constexpr int TN = T + R - 1;  // stage this step prefetches
+    constexpr bool pre = TN < NST;
+    constexpr int allowed = (R == 3 && T + 1 < NST ? Cfg::PER_STAGE : 0) + (pre ? 4 : 0);
+    uint8_t* cur = T % R == 0 ? s0 : (T % R == 1 ? s1 : s2);
+    uint8_t* nxt = TN % R == 0 ? s0 : (TN % R == 1 ? s1 : s2);
+    if constexpr (pre) load_w(wb[TN % R], wrow, (int64_t)SK * TN);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(allowed));
+    wg_barrier();
+    if constexpr (pre) stage_rows<MGT>(nxt + kp * Cfg::STAGE, src, (int64_t)SK * TN, cb);
+    mma_stage<MGT>(cur + kp * Cfg::STAGE, wb[T % R], acc, m, h);
+    ksteps_static<MGT, NST, T + 1>(wrow, src, s0, s1, s2, wb, acc, m, h, cb, kp);
+  }
+}
+
+// Operands of up to 4 expand items of one kind (up to four 16-rank MFMA
+// steps each) for one wave: A = rows of t or u (row 32 g + m of the item's
+// group), B = B' or B_sh rows of this lane's column. Loads go through buffer
+// resources, so ranks past a row's length never read past the operand.
+struct ExpBatch {
+  uint4 av[4][4], bv[4][4];
+  int32_t gi[4];
+};
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const uint16_t* uni_ptr(const uint16_t* p) {
+  const uint64_t v = (uint64_t)p;
+  return (const uint16_t*)(((uint64_t)(uint32_t)uni((int)(v >> 32)) << 32) |
+                           (uint32_t)uni((int)(uint32_t)v));
+}
+
+__device__ __forceinline__ void load_expand(const MainArgs& a, ExpBatch& eb, int ib, int i1,
+                                            int kind, int64_t ncol, int m, int h) {
+  const uint16_t* abase = kind == EXP_OWN ? a.tb : a.ub;
+  const int32_t astride = kind == EXP_OWN ? a.RT : a.r_v;
+  const rsrc_t ar = make_rsrc(abase, kind == EXP_OWN ? a.tb_bytes : a.ub_bytes);
+  // descriptors of the 4 items first (one round trip), made wave-uniform
+  int4 itm[4];
+  const uint16_t* bp[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int it = min(ib + q, i1 - 1);
+    itm[q] = a.items[it];
+    bp[q] = a.item_ptr[it];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int gi = uni(itm[q].x) >> 8;
+    const int k0 = uni(itm[q].y), nstp = uni(itm[q].z) & 0xFF, rank = uni(itm[q].z) >> 8;
+    const int lo = uni(itm[q].w) & 0xFFFF, hi = uni(itm[q].w) >> 16;
+    const int pa = 32 * gi + m;
+    const bool rowok = (ib + q < i1) && pa >= lo && pa < hi;
+    const rsrc_t br = make_rsrc(uni_ptr(bp[q]), (uint32_t)(a.d_out * rank * 2));
+    eb.gi[q] = gi;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kk = k0 + 16 * st + 8 * h;
+      const bool ok = st < nstp && kk < rank;
+      const uint4 bv = ldb16(br, (uint32_t)((ncol * rank + kk) * 2));
+      const uint4 av = ldb16(ar, (uint32_t)(((int64_t)pa * astride + kk) * 2));
+      eb.bv[q][st] = ok ? bv : make_uint4(0, 0, 0, 0);
+      eb.av[q][st] = (ok && rowok) ? av : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Row record in LDS: [0] = (s, e) pointers, [1] = (b pointer, token, flags)
+__device__ __forceinline__ const float* rec_ptr(u32x4 v, int hi) {
+  const uint64_t p = hi ? ((uint64_t)v.w << 32 | v.z) : ((uint64_t)v.y << 32 | v.x);
+  return (const float*)p;
+}
+
+// MGT = staged row groups = x row groups + g_rot delta groups; NST = 64-k
+// stages per K half when known at compile time (the K loop is then fully
+// unrolled, which keeps the compiler's tracking of the in-flight LDS fills
+// exact), 0 for a runtime count
+template <int MGT, int NST>
 __global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_decode_main(MainArgs a) {
   using Cfg = DecCfg<MGT>;
   constexpr int R = Cfg::R;
   // ring slots as separate LDS objects so the compiler can tell the slot
-  // being read from the ones the direct loads fill
+  // being read from the ones the direct loads fill; after the K loop slot0
+  // holds the row tile T and slot1 the VeRA tile V ([32 MGT][64] fp32 each)
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[2 * Cfg::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[2 * Cfg::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t slot2[R == 3 ? 2 * Cfg::STAGE : 16];
-  // per sorted row: pointers to live s, VeRA e and b (null if none)
-  __shared__ __attribute__((aligned(1024))) const float* lrow[3][256];
+  __shared__ u32x4 rec[32 * MGT][2];   // row records of the x rows
+  __shared__ int32_t vflag[MGT];       // V holds the group's VeRA product
   __shared__ int32_t last_flag;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int m = lane & 31, h = lane >> 5;
   const int cb = wave & 1, kp = wave >> 1;
   const int mgx = MGT - a.g_rot;  // x row groups
+  const int Mx = 32 * mgx;
 
   // XCD-aware tile order: work-groups are dispatched round-robin over the 8
-  // XCDs, so consecutive work indices (the S slices of one tile) are placed
-  // on one XCD, where the combine finds their partials in one L2
+  // XCDs, so consecutive work indices (the S slices of one tile) land on one
+  // XCD and share its L2 for the tile's x rows
   const int G = gridDim.x, bid = blockIdx.x;
   const int w = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
   const int c = w / a.S, kc = w - c * a.S;
@@ -469,21 +573,30 @@ k_decode_main(MainArgs a) {
   const int64_t ncol = (int64_t)c * 64 + cb * 32 + m;
   const int kw = a.k_chunk / 2;  // K per half
   const int64_t kbase = (int64_t)kc * a.k_chunk + (int64_t)kp * kw;
-  const int nst = kw / SK;
-  const uint16_t* wrow = a.W + (size_t)ncol * a.d_in + kbase + 32 * h;
+  const int nst = NST > 0 ? NST : kw / SK;
+  const WSrc wrow{make_rsrc(a.W, (uint32_t)((size_t)a.d_out * a.d_in * 2)),
+                  (uint32_t)(((size_t)ncol * a.d_in + kbase + 32 * h) * 2)};
 
+  // (0) record of the row this thread keeps for the epilogue
+  u32x4 rec0 = {0, 0, 0, 0}, rec1 = {0, 0, 0, 0};
+  if (tid < Mx) {
+    const GLOBAL u32x4* rp = (const GLOBAL u32x4*)(a.rows + tid);
+    rec0 = rp[0];
+    rec1 = rp[1];
+  }
   // (1) token of each staged row this lane fills (rows 8 (cb + 2q) + lane/8)
   int32_t tok[2 * MGT];
 #pragma unroll
   for (int q = 0; q < 2 * MGT; ++q) {
     const int r = 8 * (cb + 2 * q) + (lane >> 3);
-    tok[q] = r < 32 * mgx ? ldg(a.row_tok + r) : 0;
+    tok[q] = ldg(a.row_tok + min(r, Mx - 1));
   }
   // (2) W of the first R-1 stages (in flight while the tokens arrive)
-  uint4 w0[4], w1[4], w2[4];
-  load_w(w0, wrow, 0);
-  if constexpr (R == 3) load_w(w1, wrow, (int64_t)SK * min(1, nst - 1));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * (R - 1)));
+  // (with NST known, stages past the last are not loaded)
+  constexpr bool pre1 = R == 3 && NST != 1;
+  uint4 wb[3][4];
+  load_w(wb[0], wrow, 0);
+  if constexpr (pre1) load_w(wb[1], wrow, (int64_t)SK * min(1, nst - 1));
   // (3) row sources; rows past n read token 0 (finite, never written out)
   const uint16_t* src[2 * MGT];
   {
@@ -491,242 +604,220 @@ k_decode_main(MainArgs a) {
 #pragma unroll
     for (int q = 0; q < 2 * MGT; ++q) {
       const int r = 8 * (cb + 2 * q) + (lane >> 3);
-      const uint16_t* base =
-          r < 32 * mgx ? a.x + (size_t)(tok[q] < 0 ? 0 : tok[q]) * a.d_in
-                       : a.delta + (size_t)(r - 32 * mgx) * a.d_in;
+      const uint16_t* base = r < Mx ? a.x + (size_t)(tok[q] < 0 ? 0 : tok[q]) * a.d_in
+                                    : a.delta + (size_t)(r - Mx) * a.d_in;
       src[q] = base + kbase + 8 * piece;
     }
   }
   stage_rows<MGT>(slot0 + kp * Cfg::STAGE, src, 0, cb);
-  if constexpr (R == 3) stage_rows<MGT>(slot1 + kp * Cfg::STAGE, src, (int64_t)SK * min(1, nst - 1), cb);
-  // (4) row tables: 3 x 256 pointers = 6 KB; every wave issues two 1 KB loads
-  //     (instructions 6 and 7 repeat 4 and 5)
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int j0 = wave + 4 * jj;
-    const int j = j0 < 6 ? j0 : j0 - 2;
-    const float* const* tab = j < 2 ? a.row_s : (j < 4 ? a.row_ve : a.row_b);
-    __builtin_amdgcn_global_load_lds((const void*)(tab + 128 * (j & 1) + 2 * lane),
-                                     (lds_void*)(&lrow[j >> 1][128 * (j & 1)]), 16, 0, 0);
-  }
+  if constexpr (pre1) stage_rows<MGT>(slot1 + kp * Cfg::STAGE, src, (int64_t)SK * min(1, nst - 1), cb);
 
   f32x16 acc[MGT];
 #pragma unroll
   for (int g = 0; g < MGT; ++g) acc[g] = f32x16{};
-  float fv[MGT][16];
-  uint32_t ms[MGT], mv[MGT];
 
-  // stage 0 (peeled: after its barrier the row tables are in LDS and the
-  // per-row factors are prefetched for the epilogue)
+  // stage 0 (peeled: the row records go to LDS after its barrier)
   {
+    constexpr bool pre = NST == 0 || R - 1 < NST;
     const int64_t kn = (int64_t)SK * min(R - 1, nst - 1);
-    if constexpr (R == 3) load_w(w2, wrow, kn); else load_w(w1, wrow, kn);
-    // issued after the rows of stage 0: (R == 3: rows of stage 1), the two
-    // row-table loads, and W of stage R-1
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(R == 3 ? 2 * MGT + 6 : Cfg::WAIT));
+    if constexpr (pre) load_w(wb[R - 1], wrow, kn);
+    // issued after the rows of stage 0: (R == 3: rows of stage 1) and W of
+    // stage R-1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((pre1 ? 2 * MGT : 0) + (pre ? 4 : 0)));
     wg_barrier();
-    stage_rows<MGT>((R == 3 ? slot2 : slot1) + kp * Cfg::STAGE, src, kn, cb);
-#pragma unroll
-    for (int g = 0; g < MGT; ++g) {
-      ms[g] = mv[g] = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int p = 32 * g + 8 * (i >> 2) + 4 * h + (i & 3);
-        const bool live = g < mgx && kp == 0;
-        const float* sp = live ? lrow[0][p] : nullptr;
-        const float* vp = live ? lrow[1][p] : nullptr;
-        const float* fp = (live && sp) ? sp : ((live && vp) ? vp : a.ones);
-        fv[g][i] = ldg(fp + ncol);
-        if (live && sp) ms[g] |= 1u << i;
-        if (live && vp) mv[g] |= 1u << i;
-      }
+    if (tid < Mx) {
+      rec[tid][0] = rec0;
+      rec[tid][1] = rec1;
     }
-    mma_stage<MGT>(slot0 + kp * Cfg::STAGE, w0, acc, m, h);
+    if (tid < MGT) vflag[tid] = 0;
+    if constexpr (pre) stage_rows<MGT>((R == 3 ? slot2 : slot1) + kp * Cfg::STAGE, src, kn, cb);
+    mma_stage<MGT>(slot0 + kp * Cfg::STAGE, wb[0], acc, m, h);
   }
-  // remaining stages, unrolled by the ring depth so slots and W registers are
-  // named statically
-  if constexpr (R == 3) {
+  // remaining stages; stage t lives in ring slot t % R and W registers
+  // wb[t % R], named statically in both forms of the loop
+  if constexpr (NST > 0) {
+    ksteps_static<MGT, NST, 1>(wrow, src, slot0, slot1, slot2, wb, acc, m, h, cb, kp);
+  } else if constexpr (R == 3) {
 #pragma unroll 1
     for (int t = 1; t < nst; t += 3) {
-      kstep<MGT, 1>(t, nst, wrow, src, slot1, slot0, w1, w0, acc, m, h, cb, kp);
+      kstep<MGT>(t, nst, wrow, src, slot1, slot0, wb[1], wb[0], acc, m, h, cb, kp);
       if (t + 1 >= nst) break;
-      kstep<MGT, 2>(t + 1, nst, wrow, src, slot2, slot1, w2, w1, acc, m, h, cb, kp);
+      kstep<MGT>(t + 1, nst, wrow, src, slot2, slot1, wb[2], wb[1], acc, m, h, cb, kp);
       if (t + 2 >= nst) break;
-      kstep<MGT, 0>(t + 2, nst, wrow, src, slot0, slot2, w0, w2, acc, m, h, cb, kp);
+      kstep<MGT>(t + 2, nst, wrow, src, slot0, slot2, wb[0], wb[2], acc, m, h, cb, kp);
     }
   } else {
 #pragma unroll 1
     for (int t = 1; t < nst; t += 2) {
-      kstep<MGT, 1>(t, nst, wrow, src, slot1, slot0, w1, w0, acc, m, h, cb, kp);
+      kstep<MGT>(t, nst, wrow, src, slot1, slot0, wb[1], wb[0], acc, m, h, cb, kp);
       if (t + 1 >= nst) break;
-      kstep<MGT, 0>(t + 1, nst, wrow, src, slot0, slot1, w0, w1, acc, m, h, cb, kp);
+      kstep<MGT>(t + 1, nst, wrow, src, slot0, slot1, wb[0], wb[1], acc, m, h, cb, kp);
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // clamped tail prefetches
   wg_barrier();
 
-  // ---- K halves meet: half 1 hands its product to half 0 through LDS -------
-  float* red = reinterpret_cast<float*>(slot0);  // [cb][g][16][64]
+  // ---- epilogue ---------------------------------------------------------------
+  // this wave's expand items: own items on waves kp = 0, VeRA items on kp = 1;
+  // the first batch's operands are in flight while the K halves meet
+  const int kind = kp;
+  const int i0 = uni(a.item_off[2 * kc + kind]), i1 = uni(a.item_off[2 * kc + kind + 1]);
+  ExpBatch eb;
+  if (i0 < i1) load_expand(a, eb, i0, i1, kind, ncol, m, h);
+
+  // (a) K halves meet in T [32 MGT rows][64 columns]; accumulator element i
+  //     of group g is row 32 g + 8 (i / 4) + 4 h + i % 4, column cb 32 + m
+  float* T = reinterpret_cast<float*>(slot0);
+  float* V = reinterpret_cast<float*>(slot1);
   if (kp == 1) {
 #pragma unroll
     for (int g = 0; g < MGT; ++g)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[((cb * MGT + g) * 16 + i) * 64 + lane] = acc[g][i];
+      for (int i = 0; i < 16; ++i)
+        T[(32 * g + 8 * (i >> 2) + 4 * h + (i & 3)) * 64 + cb * 32 + m] = acc[g][i];
   }
   wg_barrier();
   if (kp == 0) {
 #pragma unroll
     for (int g = 0; g < MGT; ++g)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[g][i] += red[((cb * MGT + g) * 16 + i) * 64 + lane];
-  }
-
-  if (kp == 0) {
-    // rotated rows: group mgx + g holds delta W of x group g; fold it in
-#pragma unroll
-    for (int j = 1; j < MGT; ++j)
-#pragma unroll
-      for (int g = 0; g < j; ++g)
-        if (j - g == mgx && g < a.g_rot) acc[g] += acc[j];
-
-    // ---- epilogue ----------------------------------------------------------
-    // accumulator element i of group g: row 32 g + 8 (i / 4) + 4 h + i % 4,
-    // column ncol; this lane's A-operand row in group g is 32 g + m
-    // (a) s of each row's adapter multiplies this slice's base product
-#pragma unroll
-    for (int g = 0; g < MGT; ++g)
-#pragma unroll
       for (int i = 0; i < 16; ++i)
-        if (ms[g] & (1u << i)) acc[g][i] *= fv[g][i];
+        T[(32 * g + 8 * (i >> 2) + 4 * h + (i & 3)) * 64 + cb * 32 + m] += acc[g][i];
+  }
+  wg_barrier();
 
-    // (b) expand items of this K slice (<= 4 MFMA steps each), four at a time
-    const int it0 = a.item_off[kc], it1 = a.item_off[kc + 1];
-#pragma unroll 1
-    for (int ib = it0; ib < it1; ib += 4) {
-      uint4 av[4][4], bv[4][4];
-      int4 itm[4];
+  // (b) row pass 1: fold delta W into the rotated rows (delta row r belongs
+  //     to sorted row r; delta rows past n_rot are zero) and scale by s
+  const int q4 = tid & 15, rr = tid >> 4;  // float4 of the row, row within 16
+  const int nj = 2 * mgx;                  // passes of 16 rows over the x rows
+  const int64_t cbase = (int64_t)c * 64 + 4 * q4;
+  f32x4* T4 = reinterpret_cast<f32x4*>(T);
+  f32x4* V4 = reinterpret_cast<f32x4*>(V);
+  {
+    f32x4 s4[2 * MGT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int it = min(ib + q, it1 - 1);
-        itm[q] = a.items[it];
-        const uint16_t* bp = a.item_ptr[it];
-        const int type = itm[q].x & 0xFF, gi = itm[q].x >> 8;
-        const int pa = 32 * gi + m;
-        const int nstp = itm[q].z & 0xFF;  // 16-rank steps
-        const int rank = itm[q].z >> 8;    // own: B' row length; VeRA: r_v
-        const int lo = itm[q].w & 0xFFFF, hi = itm[q].w >> 16;
-        const bool rowok = (ib + q < it1) && pa >= lo && pa < hi;
-        const uint16_t* arow =
-            type == EXP_OWN ? a.tb + (size_t)pa * a.RT : a.ub + (size_t)pa * a.r_v;
-        const uint16_t* brow = bp + (size_t)ncol * rank;
+    for (int j = 0; j < 2 * MGT; ++j) {
+      const int r = rr + 16 * min(j, nj - 1);
+      s4[j] = ldg4(rec_ptr(rec[r][0], 0) + cbase);
+    }
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kk = itm[q].y + 16 * st + 8 * h;
-          const bool ok = st < nstp && kk < rank;
-          bv[q][st] = ok ? ldg16(brow + kk) : make_uint4(0, 0, 0, 0);
-          av[q][st] = (ok && rowok) ? ldg16(arow + kk) : make_uint4(0, 0, 0, 0);
-        }
+    for (int j = 0; j < 2 * MGT; ++j) {
+      if (j < nj) {
+        const int r = rr + 16 * j;
+        f32x4 v = T4[r * 16 + q4];
+        if (j < 2 * a.g_rot) v += T4[(Mx + r) * 16 + q4];
+        T4[r * 16 + q4] = v * s4[j];
       }
+    }
+  }
+  wg_barrier();
+
+  // (c) expand: own items add t B' into T; VeRA items of one row group sum
+  //     into one fragment that goes to V
+  {
+    int cg = -1;
+    f32x16 vacc = {};
+    for (int ib = i0; ib < i1; ib += 4) {
+      if (ib != i0) load_expand(a, eb, ib, i1, kind, ncol, m, h);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (ib + q >= it1) break;
-        const int type = itm[q].x & 0xFF, gi = itm[q].x >> 8;
+        if (ib + q >= i1) continue;
         f32x16 t2 = {};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) t2 = mfma32(av[q][st], bv[q][st], t2);
+        for (int st = 0; st < 4; ++st) t2 = mfma32(eb.av[q][st], eb.bv[q][st], t2);
+        const int gi = eb.gi[q];
+        if (kind == EXP_OWN) {
+          float* Tg = T + 32 * gi * 64 + cb * 32 + m;
 #pragma unroll
-        for (int g = 0; g < MGT; ++g) {
-          if (g != gi) continue;
-          if (type == EXP_OWN) {
-            acc[g] += t2;  // the own low-rank update is not scaled by s
-          } else {
+          for (int i = 0; i < 16; ++i) Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] += t2[i];
+        } else {
+          if (gi != cg) {
+            if (cg >= 0) {
+              float* Vg = V + 32 * cg * 64 + cb * 32 + m;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              if (!(mv[g] & (1u << i))) continue;
-              float e = fv[g][i];
-              if (ms[g] & (1u << i)) {  // row with both s and a VeRA term
-                const int p = 32 * g + 8 * (i >> 2) + 4 * h + (i & 3);
-                e = ldg(lrow[1][p] + ncol);
-              }
-              acc[g][i] += e * t2[i];
+              for (int i = 0; i < 16; ++i) Vg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] = vacc[i];
+              if (lane == 0) vflag[cg] = 1;
             }
+            cg = gi;
+            vacc = t2;
+          } else {
+            vacc += t2;
           }
         }
       }
     }
+    if (cg >= 0) {
+      float* Vg = V + 32 * cg * 64 + cb * 32 + m;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Vg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] = vacc[i];
+      if (lane == 0) vflag[cg] = 1;
+    }
   }
+  wg_barrier();
 
-  // ---- S slices of the tile meet ---------------------------------------------
-  bool writer = true;
-  if (a.S > 1) {
-    // partial of this slice -> workspace [slice][tile][cb][g][16][lane]
-    // through memory, wait for the stores, count arrivals; the last slice to
-    // arrive adds all slices in slice order (deterministic) and writes y
-    const size_t stride = (size_t)mgx * 16 * 64;
-    if (kp == 0) {
-      float* mine = a.part + (((size_t)kc * a.C + c) * 2 + cb) * stride + lane;
+  // (d) row pass 2: this slice's tile = T + (V (.) e) + b (b on slice 0 only)
+  f32x4 out[2 * MGT];
+  {
+    f32x4 e4[2 * MGT], b4[2 * MGT];
 #pragma unroll
-      for (int g = 0; g < MGT; ++g) {
-        if (g >= mgx) continue;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st_coh(mine + g * 1024 + 64 * i, acc[g][i]);
-      }
+    for (int j = 0; j < 2 * MGT; ++j) {
+      const int r = rr + 16 * min(j, nj - 1);
+      e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
+      b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
     }
-    wait_vm_all();
-    wg_barrier();
-    if (tid == 0) {
-      const int old = arrive(a.cnt + c);
-      last_flag = old == a.S - 1;
-      if (old == a.S - 1) reset_counter(a.cnt + c);
-    }
-    wg_barrier();
-    writer = last_flag != 0;
-    if (writer) {
-      if (kp == 0) {
-        float tot[MGT][16];
 #pragma unroll
-        for (int g = 0; g < MGT; ++g)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) tot[g][i] = 0.f;
-#pragma unroll 1
-        for (int q = 0; q < a.S; ++q) {
-          if (q == kc) {
-#pragma unroll
-            for (int g = 0; g < MGT; ++g)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) tot[g][i] += acc[g][i];
-          } else {
-            const float* pq = a.part + (((size_t)q * a.C + c) * 2 + cb) * stride + lane;
-#pragma unroll
-            for (int g = 0; g < MGT; ++g) {
-              if (g >= mgx) continue;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) tot[g][i] += ld_coh(pq + g * 1024 + 64 * i);
-            }
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < MGT; ++g)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[g][i] = tot[g][i];
-      }
+    for (int j = 0; j < 2 * MGT; ++j) {
+      const int r = rr + 16 * min(j, nj - 1);
+      f32x4 u = V4[r * 16 + q4];
+      if (!vflag[min(j, nj - 1) >> 1]) u = f32x4{0.f, 0.f, 0.f, 0.f};
+      out[j] = T4[r * 16 + q4] + u * e4[j] + b4[j];
     }
   }
 
-  // ---- shift b and y ---------------------------------------------------------
-  if (writer && kp == 0) {
+  if (a.S == 1) {
 #pragma unroll
-    for (int g = 0; g < MGT; ++g) {
-      if (g >= mgx) continue;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int p = 32 * g + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (p >= a.n) continue;
-        float v = acc[g][i];
-        const float* bp = lrow[2][p];
-        if (bp) v += ldg(bp + ncol);
-        a.y[(size_t)a.row_tok[p] * a.d_out + ncol] = v;
+    for (int j = 0; j < 2 * MGT; ++j) {
+      if (j < nj) {
+        const int tk = (int)rec[rr + 16 * j][1].z;
+        if (tk >= 0) stg4(a.y + (size_t)tk * a.d_out + cbase, out[j]);
       }
+    }
+    return;
+  }
+
+  // (e) S slices of the tile meet: store this slice's tile, wait for the
+  //     stores, count arrivals; the last slice to arrive adds every slice's
+  //     tile in slice order (slices past S read as zero) and writes y
+  const rsrc_t pr = make_rsrc(a.part, a.part_bytes);
+  const uint32_t slice_bytes = (uint32_t)a.C * (uint32_t)Mx * 256u;
+  const uint32_t tile = (uint32_t)c * (uint32_t)Mx * 256u + (uint32_t)q4 * 16u;
+#pragma unroll
+  for (int j = 0; j < 2 * MGT; ++j)
+    if (j < nj) st_sys4(pr, (uint32_t)kc * slice_bytes + tile + (uint32_t)(rr + 16 * j) * 256u, out[j]);
+  wait_vm_all();
+  wg_barrier();
+  if (tid == 0) {
+    const int old = arrive(a.cnt + c);
+    last_flag = old == a.S - 1;
+    if (old == a.S - 1) reset_counter(a.cnt + c);
+  }
+  wg_barrier();
+  if (!last_flag) return;
+  f32x4 tot[2 * MGT];
+#pragma unroll
+  for (int j = 0; j < 2 * MGT; ++j) tot[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 2 * MGT; ++j) {
+      const int r = rr + 16 * min(j, nj - 1);
+      tot[j] += ld_sys4(pr, (uint32_t)s * slice_bytes + tile + (uint32_t)r * 256u);
+    }
+#pragma unroll
+  for (int j = 0; j < 2 * MGT; ++j) {
+    if (j < nj) {
+      const int tk = (int)rec[rr + 16 * j][1].z;
+      if (tk >= 0) stg4(a.y + (size_t)tk * a.d_out + cbase, tot[j]);
     }
   }
 }
@@ -737,45 +828,42 @@ k_decode_main(MainArgs a) {
 
 template <int MGT>
 static void launch_main(const MainArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL(k_decode_main<MGT>, dim3(grid), dim3(256), 0, st, a);
+  switch (a.k_chunk / 2 / SK) {
+    case 8: hipLaunchKernelGGL((k_decode_main<MGT, 8>), dim3(grid), dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_decode_main<MGT, 32>), dim3(grid), dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_decode_main<MGT, 0>), dim3(grid), dim3(256), 0, st, a); break;
+  }
 }
 
 scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                            float* y, hipStream_t st, int32_t* launches) {
   const DecodePlan& D = B->dp;
-  ProArgs pa{};
-  pa.x = (const uint16_t*)x;
-  pa.perm = B->d_perm;
-  pa.row_adapter = B->d_row_adapter;
-  pa.vera_pos = B->d_vera_pos;
-  pa.table = L->table_dev;
-  pa.A_sh = (const uint16_t*)L->A_sh;
-  pa.y = y;
-  pa.y_vec4 = (int64_t)B->n * L->d_out / 4;
-  pa.zero_y = 0;
-  pa.items = D.pro_items;
-  pa.n_items = D.n_pro;
-  pa.tb = D.tb;
-  pa.RT = D.RT;
-  pa.ub = D.ub;
-  pa.r_v = L->r_v;
-  pa.delta = D.delta;
-  pa.vpart = D.vpart;
-  pa.vcnt = D.vcnt;
-  pa.nvb = D.nvb;
-  pa.njb = D.njb;
-  pa.SV = D.SV;
-  pa.n_vera = B->n_vera;
-  pa.sgroups = D.sgroups;
-  pa.spart = D.spart;
-  pa.scnt = D.scnt;
-  pa.n_sgroups = D.n_sgroups;
-  pa.KQ = D.KQ;
-  pa.d_in = (int32_t)L->d_in;
   int nl = 0;
-  if (pa.zero_y || pa.n_items > 0) {
-    int grid = std::max(1, std::min(2048, (pa.n_items + 3) / 4));
-    if (pa.zero_y) grid = std::max(grid, 256);
+  if (D.n_pro > 0) {
+    ProArgs pa{};
+    pa.x = (const uint16_t*)x;
+    pa.items = D.pro_items;
+    pa.n_items = D.n_pro;
+    pa.vrows = D.vrows;
+    pa.A_sh = (const uint16_t*)L->A_sh;
+    pa.tb = D.tb;
+    pa.RT = D.RT;
+    pa.ub = D.ub;
+    pa.r_v = L->r_v;
+    pa.delta = D.delta;
+    pa.spart = D.spart;
+    pa.scnt = D.scnt;
+    pa.spart_bytes = D.spart_bytes;
+    pa.n_sgroups = D.n_sgroups;
+    pa.KQ = D.KQ;
+    pa.vpart = D.vpart;
+    pa.vcnt = D.vcnt;
+    pa.vpart_bytes = D.vpart_bytes;
+    pa.nvb = D.nvb;
+    pa.njb = D.njb;
+    pa.SV = D.SV;
+    pa.d_in = (int32_t)L->d_in;
+    const int grid = std::max(1, std::min(2048, (pa.n_items + 3) / 4));
     ProfScope ps(L, st, "decode_prologue");
     hipLaunchKernelGGL(k_decode_prologue, dim3(grid), dim3(256), 0, st, pa);
     ++nl;
@@ -787,25 +875,25 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.W = (const uint16_t*)W;
   ma.delta = D.delta;
   ma.row_tok = D.row_tok;
-  ma.row_s = D.row_s;
-  ma.row_b = D.row_b;
-  ma.row_ve = D.row_ve;
+  ma.rows = D.rows;
   ma.items = D.exp_items;
   ma.item_ptr = D.exp_ptr;
   ma.item_off = D.exp_off;
   ma.tb = D.tb;
   ma.ub = D.ub;
-  ma.ones = D.ones;
+  ma.zeros = D.zeros;
   ma.part = D.part;
   ma.cnt = D.cnt;
-  ma.C = D.C;
   ma.y = y;
-  ma.n = B->n;
+  ma.tb_bytes = D.tb_bytes;
+  ma.ub_bytes = D.ub_bytes;
+  ma.part_bytes = D.part_bytes;
   ma.g_rot = D.g_rot;
   ma.d_in = (int32_t)L->d_in;
   ma.d_out = (int32_t)L->d_out;
   ma.k_chunk = D.k_chunk;
   ma.S = D.S;
+  ma.C = D.C;
   ma.RT = D.RT;
   ma.r_v = L->r_v;
   const int grid = D.C * D.S;
@@ -819,7 +907,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
     case 7: launch_main<7>(ma, grid, st); break;
     case 8: launch_main<8>(ma, grid, st); break;
     case 9: launch_main<9>(ma, grid, st); break;
-    default: return fail(SCUTE_E_UNSUPPORTED, "decode path: too many staged row groups");
+    default: return fail(SCUTE_E_UNSUPPORTED, "decode path: unsupported staged row groups");
   }
   ++nl;
   hipError_t e = hipGetLastError();

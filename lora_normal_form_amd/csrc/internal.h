@@ -79,38 +79,73 @@ struct scute_layer {
 namespace scute {
 
 // Tables and workspaces of the MFMA decode path (bf16, small batches).
+// Row of a decode batch (sorted position) as the main kernel's epilogue
+// reads it: the factor vectors of the row's adapter, with shared dummies
+// (ones for s and e, zeros for b) where the slot is absent, so every row is
+// handled by the same branch-free code. 32 bytes.
+struct DecRow {
+  const float* s;   // live s, or ones
+  const float* e;   // VeRA e, or ones
+  const float* b;   // shift b, or zeros
+  int32_t tok;      // token written by the row, -1 past n
+  int32_t flags;    // 1: the row has a VeRA term
+};
+
+// Prologue work item (one per wave), pointers and tokens resolved at plan
+// time. 48 bytes.
+//   rotation:    p0 = first sorted row, n = rows (<= 4), k = first of 64
+//                columns, tok = the rows' tokens, ptr = (R - I)^T blocks,
+//                blk = block size
+//   own shrink:  p0, n, tok as above, k = first rank | ranks (<= 4) << 16,
+//                ptr = A', blk = K part (1024 wide), grp = shrink group
+//   VeRA shrink: p0 = block of 32 VeRA rows, n = block of 32 ranks,
+//                k = K slice (512 wide)
+struct DecProItem {
+  int32_t type, p0, n, k;
+  int32_t tok[4];
+  const uint16_t* ptr;
+  int32_t blk, grp;
+};
+
+// VeRA row of a decode batch: d of its adapter, its token and sorted
+// position (-1 on padding rows, which repeat a valid token and d). 16 bytes.
+struct DecVeraRow {
+  const float* vd;
+  int32_t tok;
+  int32_t p;
+};
+
 struct DecodePlan {
   bool enabled = false;
   int32_t MG = 0;       // row groups of 32 covering the n sorted rows
   int32_t g_rot = 0;    // leading row groups that hold rotated rows
   int32_t M_pad = 0;    // 32 * MG
   int32_t RT = 0;       // row stride of tb (max own rank rounded up to 16)
-  int32_t S = 1;        // K splits of the base GEMM
+  int32_t S = 1;        // K slices of the base GEMM (1, 2 or 4)
   int32_t C = 0;        // column tiles of 64 outputs
   int32_t k_chunk = 0;  // d_in / S
   int32_t n_pro = 0;    // prologue work items
   int32_t nvb = 0, njb = 0, SV = 0;  // VeRA shrink blocking (K slices of 512)
-  const int32_t* row_tok = nullptr;  // [M_pad] token index, -1 past n
-  const float* const* row_s = nullptr;   // [256] live s of the row's adapter or null
-  const float* const* row_b = nullptr;   // [256] shift b or null
-  const float* const* row_ve = nullptr;  // [256] VeRA e or null
-  const int4* pro_items = nullptr;   // [n_pro]
-  const int4* exp_items = nullptr;   // expand items grouped by K split
+  int32_t n_sgroups = 0, KQ = 0;     // own-term shrink groups, K parts of 1024
+  int32_t n_exp = 0;
+  const int32_t* row_tok = nullptr;      // [M_pad] token staged for the row (-1 past n)
+  const DecRow* rows = nullptr;          // [M_pad]
+  const DecProItem* pro_items = nullptr; // [n_pro]
+  const DecVeraRow* vrows = nullptr;     // [32 nvb]
+  const int4* exp_items = nullptr;       // expand items by slice, own then VeRA
   const uint16_t* const* exp_ptr = nullptr;  // per expand item: B' or B_sh
-  const int32_t* exp_off = nullptr;  // [S + 1]
-  const float* ones = nullptr;  // [d_out] of 1.0f
+  const int32_t* exp_off = nullptr;      // [2 S + 1]
+  const float* zeros = nullptr;          // [d_out] of 0.0f
   uint16_t* tb = nullptr;     // [M_pad][RT] bf16 own-term shrink
   uint16_t* ub = nullptr;     // [M_pad][r_v] bf16 VeRA shrink (times d)
-  uint16_t* delta = nullptr;  // [32 * g_rot][d_in] bf16 x (R - I)
-  float* vpart = nullptr;     // [SV][nvb * njb][1024] VeRA shrink partials
+  uint16_t* delta = nullptr;  // [32 g_rot][d_in] bf16 x (R - I)
+  float* vpart = nullptr;     // [SV][nvb * njb][16][64] VeRA shrink partials
   int32_t* vcnt = nullptr;    // [nvb * njb] arrival counters (kept at zero)
-  int32_t n_exp = 0;
-  const int4* sgroups = nullptr;  // own-term shrink groups
-  float* spart = nullptr;     // [KQ][n_sgroups][16] shrink partials
-  int32_t* scnt = nullptr;    // [n_sgroups] shrink arrival counters
-  int32_t n_sgroups = 0, KQ = 0;
-  float* part = nullptr;      // [S][C][2][MG][16][64] split-K partials (S > 1)
+  float* spart = nullptr;     // [KQ][n_sgroups][16] own-shrink partials
+  int32_t* scnt = nullptr;    // [n_sgroups] arrival counters (kept at zero)
+  float* part = nullptr;      // [S][C][M_pad][64] split-K partial tiles (S > 1)
   int32_t* cnt = nullptr;     // [C] arrival counters (kept at zero)
+  uint32_t tb_bytes = 0, ub_bytes = 0, vpart_bytes = 0, spart_bytes = 0, part_bytes = 0;
 };
 
 }  // namespace scute

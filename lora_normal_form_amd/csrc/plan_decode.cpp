@@ -2,18 +2,20 @@
 //
 // The base GEMM y = (x W + delta W) (.) s + b is split into column tiles of
 // 64 outputs and S slices of the K dimension; the last slice of a tile to
-// finish adds the others' partial products (kept in a workspace) and writes
-// y once. The low-rank work of the expand step ("Where is
-// the cheapest place to compute the remaining slots?", paper-daily.com
-// explainer of "Scute: Exact Batched Serving for PEFT Adapters Beyond LoRA":
-// the expand works on tiles that each belong to one adapter; VeRA's shared
-// B is applied to every VeRA row of the batch at once) is cut into items:
-//   own item   (row group g, adapter, 16 ranks): one 32x32x16 MFMA step
-//   VeRA item  (row group g): r_v / 16 MFMA steps against the shared B_sh,
-//              then each row scaled by its adapter's e
-// and the items of every column tile are spread over its S slices.
+// finish adds the others' partial tiles (kept in a workspace) and writes y
+// once. The low-rank work of the expand step ("Where is the cheapest place
+// to compute the remaining slots?", paper-daily.com explainer of "Scute:
+// Exact Batched Serving for PEFT Adapters Beyond LoRA": the expand works on
+// tiles that each belong to one adapter; VeRA's shared B is applied to every
+// VeRA row of the batch at once) is cut into items of up to four 16-rank
+// MFMA steps:
+//   own item   (row group g, adapter segment, 64 ranks) against B'
+//   VeRA item  (row group g, 64 ranks) against the shared B_sh
+// Each K slice of a tile takes a share of both kinds; own items run on the
+// tile's first two waves, VeRA items on the other two.
 // The prologue items (rotation, own-term shrink, VeRA shrink) are listed
-// here too; see decode.hip for the kernels.
+// here too, with every pointer and token resolved; see decode.hip for the
+// kernels.
 
 #include <string.h>
 
@@ -44,7 +46,10 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const int64_t d_in = L->d_in, d_out = L->d_out;
   if (env_int("SCUTE_DECODE", 1) == 0) return SCUTE_OK;
   if (L->act != SCUTE_BF16 || n <= 0 || n > 256) return SCUTE_OK;
-  if (d_in % 128 != 0 || d_out % 64 != 0) return SCUTE_OK;
+  // K parts of the shrinks: at most 8 of 1024 (own) and 16 of 512 (VeRA)
+  if (d_in % 128 != 0 || d_in > 8192 || d_out % 64 != 0) return SCUTE_OK;
+  // W is addressed through a buffer range with 32-bit offsets
+  if (d_in * d_out * 2 >= ((int64_t)1 << 32)) return SCUTE_OK;
   if (B->n_vera > 0 && (L->r_v % 32 != 0 || d_in % 512 != 0)) return SCUTE_OK;
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const SlotEntry& E = L->table[B->seg[3 * i]];
@@ -56,7 +61,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   // two staged groups compile badly (accumulator copies); pad with one row
   // group of unused rows instead
   if (D.MG + D.g_rot == 2) D.MG += 1;
-  if (D.MG + D.g_rot > 9) {  // two LDS buffers of 32 (MG + g_rot) rows x 256 B + row tables
+  if (D.MG + D.g_rot > 9) {  // LDS: two ring slots of 32 (MG + g_rot) rows x 256 B + row records
     D = DecodePlan{};
     return SCUTE_OK;
   }
@@ -64,64 +69,37 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   D.RT = (B->max_rank + 15) / 16 * 16;
   D.C = (int32_t)(d_out / 64);
   // K slices: none when the column tiles alone nearly fill the chip (every
-  // slice costs a partial product of the whole tile in the workspace);
-  // otherwise the fewest that reach one work-group per compute unit. Each
-  // slice is split in two K halves of 64-wide stages.
+  // slice costs a partial tile in the workspace); otherwise the fewest (up
+  // to 4) that reach one work-group per compute unit. Each slice is split in
+  // two K halves of 64-wide stages.
   const int32_t cu = L->num_cu > 0 ? L->num_cu : 256;
   int32_t S = 1;
   if ((int64_t)D.C * 4 < (int64_t)cu * 3)
-    while ((int64_t)D.C * S < cu && d_in % ((int64_t)S * 2 * 128) == 0) S *= 2;
+    while (S < 4 && (int64_t)D.C * S < cu && d_in % ((int64_t)S * 2 * 128) == 0) S *= 2;
   S = env_int("SCUTE_DECODE_SPLITK", S);
-  if (S < 1 || d_in % ((int64_t)S * 128) != 0)
-    return fail(SCUTE_E_INVALID, "bad SCUTE_DECODE_SPLITK");
+  if ((S != 1 && S != 2 && S != 4) || d_in % ((int64_t)S * 128) != 0)
+    return fail(SCUTE_E_INVALID, "bad SCUTE_DECODE_SPLITK (1, 2 or 4 dividing d_in / 128)");
   D.S = S;
   D.k_chunk = (int32_t)(d_in / S);
 
-  // ---- per-row tables (pointer tables padded to 256 rows) --------------------
-  std::vector<int32_t> row_tok(D.M_pad, -1);
-  std::vector<const float*> row_s(256, nullptr), row_b(256, nullptr), row_ve(256, nullptr);
-  for (int32_t p = 0; p < n; ++p) {
-    row_tok[p] = B->perm[p];
-    int32_t a = B->row_adapter[p];
-    if (a < 0) continue;
-    const SlotEntry& E = L->table[a];
-    if (E.flags & F_S) row_s[p] = E.s;
-    if (E.flags & F_B) row_b[p] = E.b;
-    if (E.flags & F_VERA) row_ve[p] = E.ve;
-  }
-
-  // ---- prologue items -------------------------------------------------------
-  //   rotation: (first row, rows <= 4, first of 64 columns)
-  //   own shrink: (group of <= 4 rows x <= 4 ranks, K part of 1024)
-  //   VeRA shrink: (32-row block of VeRA rows, 32-row block of A_sh, K slice of 512)
-  std::vector<int4> pro, sgroups;
+  // ---- counts that size the tables ------------------------------------------
+  int32_t n_rot_items = 0, n_sgroups = 0;
   for (int32_t i = 0; i < B->nseg(); ++i) {
-    const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
+    const int32_t a = B->seg[3 * i], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
-    if (E.flags & F_R)
-      for (int32_t r0 = 0; r0 < len; r0 += 4)
-        for (int64_t c0 = 0; c0 < d_in; c0 += 64)
-          pro.push_back(make_int4(PRO_ROT, start + r0, std::min(4, len - r0), (int32_t)c0));
-    if (E.flags & F_TERM)
-      for (int32_t r0 = 0; r0 < len; r0 += 4)
-        for (int32_t k = 0; k < E.rank; k += 4)
-          sgroups.push_back(make_int4(start + r0, std::min(4, len - r0), k, std::min(4, E.rank - k)));
+    if (E.flags & F_R) n_rot_items += (len + 3) / 4 * (int32_t)(d_in / 64);
+    if (E.flags & F_TERM) n_sgroups += (len + 3) / 4 * ((E.rank + 3) / 4);
   }
   D.KQ = (int32_t)((d_in + 1023) / 1024);
-  D.n_sgroups = (int32_t)sgroups.size();
-  for (int32_t kq = 0; kq < D.KQ; ++kq)
-    for (int32_t gi = 0; gi < D.n_sgroups; ++gi) pro.push_back(make_int4(PRO_SHRINK, gi, kq, 0));
+  D.n_sgroups = n_sgroups;
   if (B->n_vera > 0) {
     D.nvb = (B->n_vera + 31) / 32;
     D.njb = L->r_v / 32;
     D.SV = (int32_t)(d_in / 512);
-    for (int32_t kv = 0; kv < D.SV; ++kv)
-      for (int32_t vb = 0; vb < D.nvb; ++vb)
-        for (int32_t jb = 0; jb < D.njb; ++jb) pro.push_back(make_int4(PRO_VSHRINK, vb, jb, kv));
   }
-  D.n_pro = (int32_t)pro.size();
+  const int32_t n_pro = n_rot_items + D.KQ * n_sgroups + D.SV * D.nvb * D.njb;
 
-  // ---- expand items, spread over the S K-slices -----------------------------
+  // ---- expand items ----------------------------------------------------------
   // item: (type | row group << 8, first rank, 16-rank steps (<= 4) | B row
   // length << 8, first row | end row << 16), plus the B pointer
   struct Item {
@@ -129,56 +107,77 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     const uint16_t* ptr;
     int32_t cost;
   };
-  std::vector<Item> items;
+  std::vector<Item> own_items, vera_items;
+  std::vector<int32_t> row_vera(D.M_pad, 0);
+  for (int32_t p = 0; p < n; ++p) {
+    const int32_t a = B->row_adapter[p];
+    if (a >= 0 && (L->table[a].flags & F_VERA)) row_vera[p] = 1;
+  }
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
     if (!(E.flags & F_TERM)) continue;
     for (int32_t g = start / 32; g * 32 < start + len; ++g) {
-      int32_t lo = std::max(start, 32 * g), hi = std::min(start + len, 32 * g + 32);
+      const int32_t lo = std::max(start, 32 * g), hi = std::min(start + len, 32 * g + 32);
       for (int32_t k = 0; k < E.rank; k += 64) {
-        int32_t nst = std::min(4, (E.rank - k + 15) / 16);
-        items.push_back({make_int4(EXP_OWN | (g << 8), k, nst | (E.rank << 8), lo | (hi << 16)),
-                         (const uint16_t*)E.B, nst});
+        const int32_t nst = std::min(4, (E.rank - k + 15) / 16);
+        own_items.push_back({make_int4(EXP_OWN | (g << 8), k, nst | (E.rank << 8), lo | (hi << 16)),
+                             (const uint16_t*)E.B, nst});
       }
     }
   }
   if (B->n_vera > 0) {
     for (int32_t g = 0; g < D.MG; ++g) {
       bool any = false;
-      for (int32_t p = 32 * g; p < std::min(n, 32 * g + 32); ++p) any |= row_ve[p] != nullptr;
+      for (int32_t p = 32 * g; p < std::min(n, 32 * g + 32); ++p) any |= row_vera[p] != 0;
       if (!any) continue;
       for (int32_t k = 0; k < L->r_v; k += 64) {
-        int32_t nst = std::min(4, (L->r_v - k) / 16);
-        items.push_back({make_int4(EXP_VERA | (g << 8), k, nst | (L->r_v << 8),
-                                   (32 * g) | ((32 * g + 32) << 16)),
-                         (const uint16_t*)L->B_sh, nst + 2});
+        const int32_t nst = std::min(4, (L->r_v - k) / 16);
+        vera_items.push_back({make_int4(EXP_VERA | (g << 8), k, nst | (L->r_v << 8),
+                                        (32 * g) | ((32 * g + 32) << 16)),
+                              (const uint16_t*)L->B_sh, nst});
       }
     }
   }
-  std::stable_sort(items.begin(), items.end(),
-                   [](const Item& p, const Item& q) { return p.cost > q.cost; });
-  std::vector<std::vector<Item>> per(S);
-  std::vector<int64_t> load(S, 0);
-  for (const Item& it : items) {
-    int32_t best = (int32_t)(std::min_element(load.begin(), load.end()) - load.begin());
-    per[best].push_back(it);
-    load[best] += it.cost;
-  }
+  // spread each kind over the S slices (greedy by cost); VeRA items of a
+  // slice stay ordered by row group so one wave sums a group's items before
+  // storing it
+  auto spread = [&](std::vector<Item>& items, bool by_group) {
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& p, const Item& q) { return p.cost > q.cost; });
+    std::vector<std::vector<Item>> per(S);
+    std::vector<int64_t> load(S, 0);
+    for (const Item& it : items) {
+      const int32_t best = (int32_t)(std::min_element(load.begin(), load.end()) - load.begin());
+      per[best].push_back(it);
+      load[best] += it.cost;
+    }
+    if (by_group)
+      for (auto& v : per)
+        std::stable_sort(v.begin(), v.end(),
+                         [](const Item& p, const Item& q) { return (p.v.x >> 8) < (q.v.x >> 8); });
+    return per;
+  };
+  const auto own_per = spread(own_items, false), vera_per = spread(vera_items, true);
   std::vector<int4> exp;
   std::vector<const uint16_t*> exp_ptr;
-  std::vector<int32_t> exp_off(S + 1, 0);
+  std::vector<int32_t> exp_off(2 * S + 1, 0);
   for (int32_t k = 0; k < S; ++k) {
-    exp_off[k] = (int32_t)exp.size();
-    for (const Item& it : per[k]) {
+    exp_off[2 * k] = (int32_t)exp.size();
+    for (const Item& it : own_per[k]) {
+      exp.push_back(it.v);
+      exp_ptr.push_back(it.ptr);
+    }
+    exp_off[2 * k + 1] = (int32_t)exp.size();
+    for (const Item& it : vera_per[k]) {
       exp.push_back(it.v);
       exp_ptr.push_back(it.ptr);
     }
   }
-  exp_off[S] = (int32_t)exp.size();
+  exp_off[2 * S] = (int32_t)exp.size();
   D.n_exp = (int32_t)exp.size();
 
-  // ---- one device allocation: tables, then workspaces -----------------------
+  // ---- one device allocation: tables, then zeroed workspaces -------------------
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t r = o;
@@ -186,71 +185,172 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     return r;
   };
   const size_t o_tok = take(4 * (size_t)D.M_pad);
-  const size_t o_s = take(8 * 256), o_b = take(8 * 256), o_ve = take(8 * 256);
-  const size_t o_pro = take(16 * pro.size() + 16), o_exp = take(16 * exp.size() + 16);
+  const size_t o_rows = take(sizeof(DecRow) * (size_t)D.M_pad);
+  const size_t o_pro = take(sizeof(DecProItem) * (size_t)n_pro + 16);
+  const size_t o_vrows = take(sizeof(DecVeraRow) * 32 * (size_t)D.nvb + 16);
+  const size_t o_exp = take(16 * exp.size() + 16);
   const size_t o_ptr = take(8 * exp_ptr.size() + 8);
   const size_t o_off = take(4 * exp_off.size());
-  const size_t o_sg = take(16 * sgroups.size() + 16);
   const size_t o_ones = take(4 * (size_t)d_out);
   const size_t tables = o;
-  const size_t o_tb = take(2 * (size_t)D.M_pad * D.RT);
-  const size_t o_ub = take(B->n_vera ? 2 * (size_t)D.M_pad * L->r_v : 0);
+  const size_t o_zeros = take(4 * (size_t)d_out);
+  const size_t tb_bytes = 2 * (size_t)D.M_pad * D.RT;
+  const size_t ub_bytes = B->n_vera ? 2 * (size_t)D.M_pad * L->r_v : 0;
+  const size_t vpart_bytes = 4 * (size_t)D.SV * D.nvb * D.njb * 1024;
+  const size_t spart_bytes = 4 * (size_t)D.KQ * n_sgroups * 16;
+  const size_t part_bytes = S > 1 ? 4 * (size_t)S * D.C * D.M_pad * 64 : 0;
+  if (part_bytes >= ((size_t)1 << 31) || vpart_bytes >= ((size_t)1 << 31)) {
+    D = DecodePlan{};  // buffer offsets are 32-bit
+    return SCUTE_OK;
+  }
+  const size_t o_tb = take(tb_bytes), o_ub = take(ub_bytes);
   const size_t o_delta = take(2 * (size_t)32 * D.g_rot * d_in);
-  const size_t o_vpart = take(4 * (size_t)D.SV * D.nvb * D.njb * 1024);  // K slices of 256
-  const size_t o_vcnt = take(4 * (size_t)D.nvb * D.njb);
-  const size_t o_part = take(S > 1 ? 4 * (size_t)S * D.C * 2 * D.MG * 16 * 64 : 0);
-  const size_t o_cnt = take(4 * (size_t)D.C);
-  const size_t o_spart = take(4 * (size_t)D.KQ * D.n_sgroups * 16);
-  const size_t o_scnt = take(4 * (size_t)D.n_sgroups);
+  const size_t o_vpart = take(vpart_bytes), o_vcnt = take(4 * (size_t)D.nvb * D.njb);
+  const size_t o_spart = take(spart_bytes), o_scnt = take(4 * (size_t)n_sgroups);
+  const size_t o_part = take(part_bytes), o_cnt = take(4 * (size_t)D.C);
   const size_t total = o;
+
+  hipError_t e = hipMalloc(&B->fast_dev, total);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(decode plan)");
+  uint8_t* d = (uint8_t*)B->fast_dev;
+  const float* ones = (const float*)(d + o_ones);
+  const float* zeros = (const float*)(d + o_zeros);
+
+  // ---- per-row tables ----------------------------------------------------------
+  std::vector<int32_t> row_tok(D.M_pad, -1);
+  std::vector<DecRow> rows(D.M_pad, DecRow{ones, ones, zeros, -1, 0});
+  for (int32_t p = 0; p < n; ++p) {
+    row_tok[p] = B->perm[p];
+    rows[p].tok = B->perm[p];
+    const int32_t a = B->row_adapter[p];
+    if (a < 0) continue;
+    const SlotEntry& E = L->table[a];
+    if (E.flags & F_S) rows[p].s = E.s;
+    if (E.flags & F_B) rows[p].b = E.b;
+    if (E.flags & F_VERA) {
+      rows[p].e = E.ve;
+      rows[p].flags = 1;
+    }
+  }
+
+  // ---- prologue items -----------------------------------------------------------
+  std::vector<DecProItem> pro;
+  pro.reserve(n_pro);
+  auto toks = [&](DecProItem& it) {
+    for (int32_t r = 0; r < 4; ++r) it.tok[r] = B->perm[it.p0 + std::min(r, it.n - 1)];
+  };
+  std::vector<DecProItem> shrink_groups;
+  for (int32_t i = 0; i < B->nseg(); ++i) {
+    const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
+    const SlotEntry& E = L->table[a];
+    if (E.flags & F_R)
+      for (int32_t r0 = 0; r0 < len; r0 += 4)
+        for (int64_t c0 = 0; c0 < d_in; c0 += 64) {
+          DecProItem it{};
+          it.type = PRO_ROT;
+          it.p0 = start + r0;
+          it.n = std::min(4, len - r0);
+          it.k = (int32_t)c0;
+          toks(it);
+          it.ptr = (const uint16_t*)E.P;
+          it.blk = E.blk;
+          pro.push_back(it);
+        }
+    if (E.flags & F_TERM)
+      for (int32_t r0 = 0; r0 < len; r0 += 4)
+        for (int32_t k = 0; k < E.rank; k += 4) {
+          DecProItem it{};
+          it.type = PRO_SHRINK;
+          it.p0 = start + r0;
+          it.n = std::min(4, len - r0);
+          it.k = k | (std::min(4, E.rank - k) << 16);
+          toks(it);
+          it.ptr = (const uint16_t*)E.A;
+          it.grp = (int32_t)shrink_groups.size();
+          shrink_groups.push_back(it);
+        }
+  }
+  for (int32_t kq = 0; kq < D.KQ; ++kq)
+    for (DecProItem it : shrink_groups) {
+      it.blk = kq;
+      pro.push_back(it);
+    }
+  std::vector<DecVeraRow> vrows;
+  if (B->n_vera > 0) {
+    for (int32_t kv = 0; kv < D.SV; ++kv)
+      for (int32_t vb = 0; vb < D.nvb; ++vb)
+        for (int32_t jb = 0; jb < D.njb; ++jb) {
+          DecProItem it{};
+          it.type = PRO_VSHRINK;
+          it.p0 = vb;
+          it.n = jb;
+          it.k = kv;
+          pro.push_back(it);
+        }
+    vrows.resize(32 * (size_t)D.nvb);
+    for (size_t v = 0; v < vrows.size(); ++v) {
+      const bool real = v < (size_t)B->n_vera;
+      const int32_t p = B->vera_pos[real ? v : 0];
+      vrows[v].vd = L->table[B->row_adapter[p]].vd;
+      vrows[v].tok = B->perm[p];
+      vrows[v].p = real ? p : -1;
+    }
+  }
+  D.n_pro = (int32_t)pro.size();
+  if (D.n_pro != n_pro) {
+    (void)hipFree(B->fast_dev);
+    B->fast_dev = nullptr;
+    D = DecodePlan{};
+    return fail(SCUTE_E_STATE, "decode plan: prologue item count mismatch");
+  }
 
   std::vector<uint8_t> h(tables, 0);
   memcpy(h.data() + o_tok, row_tok.data(), 4 * row_tok.size());
-  memcpy(h.data() + o_s, row_s.data(), 8 * row_s.size());
-  memcpy(h.data() + o_b, row_b.data(), 8 * row_b.size());
-  memcpy(h.data() + o_ve, row_ve.data(), 8 * row_ve.size());
-  if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), 16 * pro.size());
+  memcpy(h.data() + o_rows, rows.data(), sizeof(DecRow) * rows.size());
+  if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), sizeof(DecProItem) * pro.size());
+  if (!vrows.empty()) memcpy(h.data() + o_vrows, vrows.data(), sizeof(DecVeraRow) * vrows.size());
   if (!exp.empty()) memcpy(h.data() + o_exp, exp.data(), 16 * exp.size());
   if (!exp_ptr.empty()) memcpy(h.data() + o_ptr, exp_ptr.data(), 8 * exp_ptr.size());
   memcpy(h.data() + o_off, exp_off.data(), 4 * exp_off.size());
-  if (!sgroups.empty()) memcpy(h.data() + o_sg, sgroups.data(), 16 * sgroups.size());
   for (int64_t j = 0; j < d_out; ++j) {
     const float one = 1.0f;
     memcpy(h.data() + o_ones + 4 * j, &one, 4);
   }
 
-  hipError_t e = hipMalloc(&B->fast_dev, total);
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(decode plan)");
-  uint8_t* d = (uint8_t*)B->fast_dev;
   // workspaces start at zero: rows of delta past n_rot, ranks of tb past each
-  // row's own rank, and the VeRA counters must read as zero
+  // row's own rank, rows of ub without VeRA, and the arrival counters must
+  // read as zero
   e = hipMemsetAsync(d + tables, 0, total - tables, st);
   if (e == hipSuccess) e = hipMemcpyAsync(d, h.data(), tables, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     (void)hipFree(B->fast_dev);
     B->fast_dev = nullptr;
+    D = DecodePlan{};
     return hip_fail(e, "upload decode plan");
   }
   D.row_tok = (const int32_t*)(d + o_tok);
-  D.row_s = (const float* const*)(d + o_s);
-  D.row_b = (const float* const*)(d + o_b);
-  D.row_ve = (const float* const*)(d + o_ve);
-  D.pro_items = (const int4*)(d + o_pro);
+  D.rows = (const DecRow*)(d + o_rows);
+  D.pro_items = (const DecProItem*)(d + o_pro);
+  D.vrows = B->n_vera ? (const DecVeraRow*)(d + o_vrows) : nullptr;
   D.exp_items = (const int4*)(d + o_exp);
   D.exp_ptr = (const uint16_t* const*)(d + o_ptr);
   D.exp_off = (const int32_t*)(d + o_off);
-  D.ones = (const float*)(d + o_ones);
+  D.zeros = zeros;
   D.tb = D.RT ? (uint16_t*)(d + o_tb) : nullptr;
   D.ub = B->n_vera ? (uint16_t*)(d + o_ub) : nullptr;
   D.delta = D.g_rot ? (uint16_t*)(d + o_delta) : nullptr;
   D.vpart = B->n_vera ? (float*)(d + o_vpart) : nullptr;
   D.vcnt = B->n_vera ? (int32_t*)(d + o_vcnt) : nullptr;
-  D.part = S > 1 ? (float*)(d + o_part) : nullptr;
-  D.cnt = (int32_t*)(d + o_cnt);
-  D.sgroups = (const int4*)(d + o_sg);
   D.spart = (float*)(d + o_spart);
   D.scnt = (int32_t*)(d + o_scnt);
+  D.part = S > 1 ? (float*)(d + o_part) : nullptr;
+  D.cnt = (int32_t*)(d + o_cnt);
+  D.tb_bytes = (uint32_t)tb_bytes;
+  D.ub_bytes = (uint32_t)ub_bytes;
+  D.vpart_bytes = (uint32_t)vpart_bytes;
+  D.spart_bytes = (uint32_t)spart_bytes;
+  D.part_bytes = (uint32_t)part_bytes;
   D.enabled = true;
   return SCUTE_OK;
 }
