@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overhead", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", type=float, default=0.0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (HBM-counter calibration)")
     return ap.parse_args()
 
 
@@ -111,6 +113,33 @@ def dominant_kernel_bytes(name, wl, cost):
     return None
 
 
+def measured_traffic(kernel, wl):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary
+    for this workload, or None when there is none or the kernel sources have
+    changed since the counters were taken."""
+    from lora_normal_form_amd import profsum
+    path = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != profsum.source_sha():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    if not k or k.get("fetch_bytes") is None or k.get("write_bytes") is None:
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
+
+
+def calib_copy(torch, mib):
+    n = int(mib * 2 ** 20) // 4
+    a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(wl, seconds):
     import numpy as np
     import oracle
@@ -178,8 +207,10 @@ def main():
         kb = dominant_kernel_bytes(dom, wl, cost)
         if kb is not None:
             ach = kb / avg_s / 1e9
+            tr = measured_traffic(dom, wl)
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                    "traffic": None if tr is None else round(tr),
                     "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 3),
                     "bytes_per_launch": kb}
 
@@ -200,6 +231,9 @@ def main():
         extra["all_lora_gbps"] = round(m1["cost"]["bytes"] / (ms1 * 1e-3) / 1e9, 1)
         extra["mixed_over_all_lora_time"] = round(ms / ms1, 4)
         del m1
+
+    if args.calib_copy > 0:
+        calib_copy(torch, args.calib_copy)
 
     cpu = None
     if not args.no_cpu_baseline:

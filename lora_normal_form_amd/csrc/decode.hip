@@ -3,18 +3,20 @@
 // Two kernels per forward.
 //
 // k_decode_prologue works on small items, one per wave:
+//   gather      copy the batch's x rows into sorted order, so the main
+//               kernel stages rows at affine addresses;
 //   rotation    delta = x (R - I) for up to 4 rotated rows and 64 columns
-//               (R is block-diagonal, so a column needs one block of x);
+//               (R is block-diagonal, so a column needs one block of x),
+//               stored after the sorted x rows;
 //   own shrink  t = x A' for up to 4 rows x 4 ranks over a K part of 1024;
 //   VeRA shrink u = (x A_sh) (.) d for 32 VeRA rows x 32 ranks over a K
 //               slice of 512, on one 32x32x16 MFMA tile.
 // Rotation runs before the shared GEMM and the shared VeRA pair is read once
 // per step for the whole batch ("Where is the cheapest place to compute the
 // remaining slots?", paper-daily.com explainer of "Scute: Exact Batched
-// Serving for PEFT Adapters Beyond LoRA"). The K parts of a shrink meet
-// through a small workspace: every part stores its partial sums and the last
-// part to arrive adds them all in K order (so the result does not depend on
-// arrival order) and writes the bf16 result.
+// Serving for PEFT Adapters Beyond LoRA"). The K parts of a shrink add into
+// an fp32 buffer with float atomics (no waiting on each other); the buffers
+// alternate between forwards and each prologue clears the other one.
 //
 // k_decode_main computes, per work-group of 4 waves, 64 output columns over
 // one of S slices of K for all rows of the batch:
@@ -127,7 +129,7 @@ __device__ __forceinline__ void reset_counter(int32_t* cnt) {
   __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2 };
+enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3 };
 enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
 
 }  // namespace
@@ -142,19 +144,11 @@ struct ProArgs {
   int32_t n_items;
   const DecVeraRow* vrows;  // [32 nvb]
   const uint16_t* A_sh;     // [r_v][d_in]
-  uint16_t* tb;             // [M_pad][RT]
-  int32_t RT;
-  uint16_t* ub;             // [M_pad][r_v]
-  int32_t r_v;
-  uint16_t* delta;          // [32 g_rot][d_in]
-  float* spart;             // [KQ][n_sgroups][16]
-  int32_t* scnt;            // [n_sgroups]
-  uint32_t spart_bytes;
-  int32_t n_sgroups, KQ;
-  float* vpart;             // [SV][nvb * njb][16][64]
-  int32_t* vcnt;            // [nvb * njb]
-  uint32_t vpart_bytes;
-  int32_t nvb, njb, SV;
+  uint16_t* xs;             // [M_pad + 32 g_rot][d_in] sorted x rows, then delta rows
+  float* acc;               // [M_pad][AW] this forward's shrink sums (zero on entry)
+  float* acc_next;          // the other buffer, cleared for the next forward
+  uint32_t acc_words;       // M_pad * AW (a multiple of 4)
+  int32_t M_pad, AW, RT;
   int32_t d_in;
 };
 
@@ -183,13 +177,35 @@ __device__ __forceinline__ void rotate_rows(const uint16_t* Pt, int32_t blk,
   }
 }
 
-__global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+// One wave per work-group, so consecutive items (the heavy VeRA-shrink items
+// come first) land on different compute units.
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+k_decode_prologue(ProArgs a) {
+  const int lane = threadIdx.x;
   const int64_t d_in = a.d_in;
-  for (int it = blockIdx.x * 4 + wave; it < a.n_items; it += gridDim.x * 4) {
+  {
+    f32x4* z = reinterpret_cast<f32x4*>(a.acc_next);
+    for (uint32_t i = blockIdx.x * 64 + lane; i < a.acc_words / 4; i += gridDim.x * 64)
+      z[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int it = blockIdx.x; it < a.n_items; it += gridDim.x) {
     const DecProItem item = a.items[it];
-    if (item.type == PRO_ROT) {
+    if (item.type == PRO_GATHER) {
+      // one x row (d_in <= 8192: at most 16 16-byte pieces per lane)
+      const uint16_t* src = a.x + (size_t)item.tok[0] * d_in;
+      uint16_t* dst = a.xs + (size_t)item.p0 * d_in;
+      u32x4 v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t c = (int64_t)lane * 8 + 512 * q;
+        if (c < d_in) v[q] = *(const GLOBAL u32x4*)(src + c);
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t c = (int64_t)lane * 8 + 512 * q;
+        if (c < d_in) *(GLOBAL u32x4*)(dst + c) = v[q];
+      }
+    } else if (item.type == PRO_ROT) {
       // delta[p][col] = sum_i x[tok p][kb blk + i] (R - I)[kb][i][col - kb blk]
       const int64_t col = (int64_t)item.k + lane;
       const int32_t blk = item.blk;
@@ -211,16 +227,16 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
             for (int r = 0; r < 4; ++r) acc[r] += bf2f(ldg(xr[r] + kb * blk + i)) * pv;
           }
         }
+        uint16_t* drow = a.xs + (size_t)(a.M_pad + item.p0) * d_in + col;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (r < item.n) a.delta[(size_t)(item.p0 + r) * d_in + col] = f2bf(acc[r]);
+          if (r < item.n) drow[(size_t)r * d_in] = f2bf(acc[r]);
       }
     } else if (item.type == PRO_SHRINK) {
       // own-term shrink t = x A' for up to 4 rows x 4 ranks over one K part
-      // of 1024; the last K part to arrive sums the parts in K order
+      // of 1024, added into the row's own-rank slots
       const int32_t len = item.n, k0 = item.k & 0xFFFF, nk = item.k >> 16;
-      const int32_t kq = item.blk, grp = item.grp;
-      const int64_t cbeg = (int64_t)kq * 1024;
+      const int64_t cbeg = (int64_t)item.blk * 1024;
       const uint16_t* ar[4];
       const uint16_t* xr[4];
 #pragma unroll
@@ -258,29 +274,13 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
           const float v = wave_sum(acc[r][j]);
           if (lane == 4 * r + j) mine = v;
         }
-      const rsrc_t pr = make_rsrc(a.spart, a.spart_bytes);
-      if (lane < 16) st_sys(pr, (uint32_t)(((kq * a.n_sgroups + grp) * 16 + lane) * 4), mine);
-      wait_vm_all();
-      int32_t old = 0;
-      if (lane == 0) old = arrive(&a.scnt[grp]);
-      old = __shfl(old, 0, 64);
-      if (old == a.KQ - 1) {
-        // parts past KQ lie past the workspace and read as zero
-        const int l16 = lane & 15;
-        float tot = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          tot += ld_sys(pr, (uint32_t)(((q * a.n_sgroups + grp) * 16 + l16) * 4));
-        const int r = l16 >> 2, j = l16 & 3;
-        if (lane < 16 && r < len && j < nk)
-          a.tb[(size_t)(item.p0 + r) * a.RT + k0 + j] = f2bf(tot);
-        if (lane == 0) reset_counter(&a.scnt[grp]);
-      }
+      const int r = lane >> 2, j = lane & 3;
+      if (lane < 16 && r < len && j < nk)
+        atomicAdd(a.acc + (size_t)(item.p0 + r) * a.AW + k0 + j, mine);
     } else {
       // VeRA shrink block: 32 VeRA rows x 32 ranks of A_sh over one K slice
-      // of 512 (two rounds of loads); each slice scales its partial by d
-      // (d is per rank, so it commutes with the K sum) and the last of the
-      // SV slices to arrive adds them in slice order
+      // of 512 (two rounds of loads), scaled by d (per rank, so it commutes
+      // with the K sum) and added into the row's VeRA slots
       const int32_t vb = item.p0, jb = item.n, kv = item.k;
       const int m = lane & 31, h = lane >> 5;
       const DecVeraRow vr = a.vrows[32 * vb + m];
@@ -308,37 +308,9 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc = mfma32(xa[q], wa[q], acc);
       }
-      const int32_t blkid = vb * a.njb + jb, nblk = a.nvb * a.njb;
-      const rsrc_t pr = make_rsrc(a.vpart, a.vpart_bytes);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        st_sys(pr, (uint32_t)((((kv * nblk + blkid) * 16 + i) * 64 + lane) * 4), acc[i] * dsc[i]);
-      wait_vm_all();
-      int32_t old = 0;
-      if (lane == 0) old = arrive(&a.vcnt[blkid]);
-      old = __shfl(old, 0, 64);
-      if (old == a.SV - 1) {
-        // slices past SV lie past the workspace and read as zero
-        float tot[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tot[i] = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            tot[i] += ld_sys(pr, (uint32_t)((((q * nblk + blkid) * 16 + i) * 64 + lane) * 4));
-        if (a.SV > 8) {
-#pragma unroll
-          for (int q = 8; q < 16; ++q)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              tot[i] += ld_sys(pr, (uint32_t)((((q * nblk + blkid) * 16 + i) * 64 + lane) * 4));
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (prow[i] >= 0) a.ub[(size_t)prow[i] * a.r_v + j] = f2bf(tot[i]);
-        if (lane == 0) reset_counter(&a.vcnt[blkid]);
-      }
+        if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + a.RT + j, acc[i] * dsc[i]);
     }
   }
 }
@@ -348,22 +320,19 @@ __global__ void __launch_bounds__(256) k_decode_prologue(ProArgs a) {
 // ---------------------------------------------------------------------------
 
 struct MainArgs {
-  const uint16_t* x;
+  const uint16_t* xs;               // [32 MGT][d_in] sorted x rows, then delta rows
   const uint16_t* W;
-  const uint16_t* delta;            // [32 g_rot][d_in]
-  const int32_t* row_tok;           // [M_pad] token staged for the row, -1 past n
   const DecRow* rows;               // [M_pad]
   const int4* items;                // expand items by slice, own then VeRA
   const uint16_t* const* item_ptr;  // per item: B' of its adapter (own) or B_sh (VeRA)
-  const int32_t* item_off;          // [2 S + 1]
-  const uint16_t* tb;               // [M_pad][RT] own-term shrink (bf16)
-  const uint16_t* ub;               // [M_pad][r_v] VeRA shrink (bf16), zero rows elsewhere
+  const float* acc;                 // [M_pad][AW] shrink sums: RT own ranks, then r_v VeRA ranks
   const float* zeros;               // [d_out]
   float* part;                      // [S][C][M_pad][64] split-K partial tiles (S > 1)
   int32_t* cnt;                     // [C] arrival counters, kept at zero between forwards
   float* y;
-  uint32_t tb_bytes, ub_bytes, part_bytes;
-  int32_t g_rot, d_in, d_out, k_chunk, S, C, RT, r_v;
+  uint32_t acc_bytes, part_bytes;
+  int32_t off[9];                   // [2 S + 1]: slice k own items [2k, 2k+1), VeRA [2k+1, 2k+2)
+  int32_t g_rot, d_in, d_out, k_chunk, S, C, RT, AW;
 };
 
 // Tile of the main kernel: 64 output columns (two 32-column MFMA blocks) by
@@ -481,9 +450,15 @@ __device__ __forceinline__ void ksteps_static(const WSrc& wrow, const uint16_t* 
 }
 
 // Operands of up to 4 expand items of one kind (up to four 16-rank MFMA
-// steps each) for one wave: A = rows of t or u (row 32 g + m of the item's
-// group), B = B' or B_sh rows of this lane's column. Loads go through buffer
-// resources, so ranks past a row's length never read past the operand.
+// steps each) for one wave: A = the rows' shrink sums (row 32 g + m of the
+// item's group, fp32 rounded to bf16), B = B' or B_sh rows of this lane's
+// column. Loads go through buffer resources, so ranks past a row's length
+// never read past the operand. The descriptors are fetched first (early, so
+// they are in registers when the operands are needed).
+struct ExpDesc {
+  int4 itm[4];
+  const uint16_t* bp[4];
+};
 struct ExpBatch {
   uint4 av[4][4], bv[4][4];
   int32_t gi[4];
@@ -495,37 +470,60 @@ __device__ __forceinline__ const uint16_t* uni_ptr(const uint16_t* p) {
   return (const uint16_t*)(((uint64_t)(uint32_t)uni((int)(v >> 32)) << 32) |
                            (uint32_t)uni((int)(uint32_t)v));
 }
+__device__ __forceinline__ uint32_t pack_bf2(uint32_t lo, uint32_t hi) {
+  return (uint32_t)f2bf(__uint_as_float(lo)) | ((uint32_t)f2bf(__uint_as_float(hi)) << 16);
+}
 
-__device__ __forceinline__ void load_expand(const MainArgs& a, ExpBatch& eb, int ib, int i1,
-                                            int kind, int64_t ncol, int m, int h) {
-  const uint16_t* abase = kind == EXP_OWN ? a.tb : a.ub;
-  const int32_t astride = kind == EXP_OWN ? a.RT : a.r_v;
-  const rsrc_t ar = make_rsrc(abase, kind == EXP_OWN ? a.tb_bytes : a.ub_bytes);
-  // descriptors of the 4 items first (one round trip), made wave-uniform
-  int4 itm[4];
-  const uint16_t* bp[4];
+__device__ __forceinline__ void fetch_desc(const MainArgs& a, ExpDesc& d, int ib, int i1) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int it = min(ib + q, i1 - 1);
-    itm[q] = a.items[it];
-    bp[q] = a.item_ptr[it];
+    d.itm[q] = a.items[it];
+    d.bp[q] = a.item_ptr[it];
+  }
+}
+
+__device__ __forceinline__ void load_operands(const MainArgs& a, const ExpDesc& d, ExpBatch& eb,
+                                              int ib, int i1, int kind, int64_t ncol, int m,
+                                              int h) {
+  const rsrc_t ar = make_rsrc(a.acc, a.acc_bytes);
+  const int32_t acol = kind == EXP_OWN ? 0 : a.RT;
+  // all loads first, conversions after, so the batch costs one round trip
+  uint4 braw[4][4], araw[4][4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int gi = uni(d.itm[q].x) >> 8;
+    const int k0 = uni(d.itm[q].y), rank = uni(d.itm[q].z) >> 8;
+    const int pa = 32 * gi + m;
+    const rsrc_t br = make_rsrc(uni_ptr(d.bp[q]), (uint32_t)(a.d_out * rank * 2));
+    const int nstp = (ib + q < i1) ? uni(d.itm[q].z) & 0xFF : 0;  // steps this item uses
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (st < nstp) {
+        const int kk = k0 + 16 * st + 8 * h;
+        braw[q][st] = ldb16(br, (uint32_t)((ncol * rank + kk) * 2));
+        const uint32_t ao = (uint32_t)(((int64_t)pa * a.AW + acol + kk) * 4);
+        araw[q][st][0] = ldb16(ar, ao);
+        araw[q][st][1] = ldb16(ar, ao + 16);
+      }
+    }
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int gi = uni(itm[q].x) >> 8;
-    const int k0 = uni(itm[q].y), nstp = uni(itm[q].z) & 0xFF, rank = uni(itm[q].z) >> 8;
-    const int lo = uni(itm[q].w) & 0xFFFF, hi = uni(itm[q].w) >> 16;
+    const int gi = uni(d.itm[q].x) >> 8;
+    const int k0 = uni(d.itm[q].y), nstp = uni(d.itm[q].z) & 0xFF, rank = uni(d.itm[q].z) >> 8;
+    const int lo = uni(d.itm[q].w) & 0xFFFF, hi = uni(d.itm[q].w) >> 16;
     const int pa = 32 * gi + m;
     const bool rowok = (ib + q < i1) && pa >= lo && pa < hi;
-    const rsrc_t br = make_rsrc(uni_ptr(bp[q]), (uint32_t)(a.d_out * rank * 2));
     eb.gi[q] = gi;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kk = k0 + 16 * st + 8 * h;
       const bool ok = st < nstp && kk < rank;
-      const uint4 bv = ldb16(br, (uint32_t)((ncol * rank + kk) * 2));
-      const uint4 av = ldb16(ar, (uint32_t)(((int64_t)pa * astride + kk) * 2));
-      eb.bv[q][st] = ok ? bv : make_uint4(0, 0, 0, 0);
+      const uint4 a0 = araw[q][st][0], a1 = araw[q][st][1];
+      const uint4 av = make_uint4(pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w),
+                                  pack_bf2(a1.x, a1.y), pack_bf2(a1.z, a1.w));
+      eb.bv[q][st] = ok ? braw[q][st] : make_uint4(0, 0, 0, 0);
       eb.av[q][st] = (ok && rowok) ? av : make_uint4(0, 0, 0, 0);
     }
   }
@@ -584,33 +582,35 @@ k_decode_main(MainArgs a) {
     rec0 = rp[0];
     rec1 = rp[1];
   }
-  // (1) token of each staged row this lane fills (rows 8 (cb + 2q) + lane/8)
-  int32_t tok[2 * MGT];
-#pragma unroll
-  for (int q = 0; q < 2 * MGT; ++q) {
-    const int r = 8 * (cb + 2 * q) + (lane >> 3);
-    tok[q] = ldg(a.row_tok + min(r, Mx - 1));
-  }
-  // (2) W of the first R-1 stages (in flight while the tokens arrive)
+  // (1) W of the first R-1 stages
   // (with NST known, stages past the last are not loaded)
   constexpr bool pre1 = R == 3 && NST != 1;
   uint4 wb[3][4];
   load_w(wb[0], wrow, 0);
   if constexpr (pre1) load_w(wb[1], wrow, (int64_t)SK * min(1, nst - 1));
-  // (3) row sources; rows past n read token 0 (finite, never written out)
+  // (2) row sources: staged row r (x rows, then delta rows) is row r of xs
   const uint16_t* src[2 * MGT];
   {
     const int piece = (lane & 7) ^ ((4 * cb + (lane >> 4)) & 7);
 #pragma unroll
     for (int q = 0; q < 2 * MGT; ++q) {
       const int r = 8 * (cb + 2 * q) + (lane >> 3);
-      const uint16_t* base = r < Mx ? a.x + (size_t)(tok[q] < 0 ? 0 : tok[q]) * a.d_in
-                                    : a.delta + (size_t)(r - Mx) * a.d_in;
-      src[q] = base + kbase + 8 * piece;
+      src[q] = a.xs + (size_t)r * a.d_in + kbase + 8 * piece;
     }
   }
   stage_rows<MGT>(slot0 + kp * Cfg::STAGE, src, 0, cb);
   if constexpr (pre1) stage_rows<MGT>(slot1 + kp * Cfg::STAGE, src, (int64_t)SK * min(1, nst - 1), cb);
+  // (3) this wave's expand items (waves kp = 0: own items, kp = 1: VeRA
+  //     items); their descriptors load now and are used after the K loop
+  const int kind = kp;
+  int i0 = 0, i1 = 0;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    if (i == 2 * kc + kind) i0 = a.off[i];
+    if (i == 2 * kc + kind + 1) i1 = a.off[i];
+  }
+  ExpDesc ed;
+  if (i0 < i1) fetch_desc(a, ed, i0, i1);
 
   f32x16 acc[MGT];
 #pragma unroll
@@ -658,12 +658,24 @@ k_decode_main(MainArgs a) {
   wg_barrier();
 
   // ---- epilogue ---------------------------------------------------------------
-  // this wave's expand items: own items on waves kp = 0, VeRA items on kp = 1;
-  // the first batch's operands are in flight while the K halves meet
-  const int kind = kp;
-  const int i0 = uni(a.item_off[2 * kc + kind]), i1 = uni(a.item_off[2 * kc + kind + 1]);
+  // the first expand batch's operands and the rows' factor vectors are in
+  // flight while the K halves meet
   ExpBatch eb;
-  if (i0 < i1) load_expand(a, eb, i0, i1, kind, ncol, m, h);
+  if (i0 < i1) load_operands(a, ed, eb, i0, i1, kind, ncol, m, h);
+  const int q4 = tid & 15, rr = tid >> 4;  // float4 of the row, row within 16
+  const int nj = 2 * mgx;                  // passes of 16 rows over the x rows
+  const int64_t cbase = (int64_t)c * 64 + 4 * q4;
+  constexpr bool early = MGT <= 6;         // register room to prefetch e and b too
+  f32x4 s4[2 * MGT], e4[2 * MGT], b4[2 * MGT];
+#pragma unroll
+  for (int j = 0; j < 2 * MGT; ++j) {
+    const int r = rr + 16 * min(j, nj - 1);
+    s4[j] = ldg4(rec_ptr(rec[r][0], 0) + cbase);
+    if constexpr (early) {
+      e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
+      b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
+    }
+  }
 
   // (a) K halves meet in T [32 MGT rows][64 columns]; accumulator element i
   //     of group g is row 32 g + 8 (i / 4) + 4 h + i % 4, column cb 32 + m
@@ -688,18 +700,9 @@ k_decode_main(MainArgs a) {
 
   // (b) row pass 1: fold delta W into the rotated rows (delta row r belongs
   //     to sorted row r; delta rows past n_rot are zero) and scale by s
-  const int q4 = tid & 15, rr = tid >> 4;  // float4 of the row, row within 16
-  const int nj = 2 * mgx;                  // passes of 16 rows over the x rows
-  const int64_t cbase = (int64_t)c * 64 + 4 * q4;
   f32x4* T4 = reinterpret_cast<f32x4*>(T);
   f32x4* V4 = reinterpret_cast<f32x4*>(V);
   {
-    f32x4 s4[2 * MGT];
-#pragma unroll
-    for (int j = 0; j < 2 * MGT; ++j) {
-      const int r = rr + 16 * min(j, nj - 1);
-      s4[j] = ldg4(rec_ptr(rec[r][0], 0) + cbase);
-    }
 #pragma unroll
     for (int j = 0; j < 2 * MGT; ++j) {
       if (j < nj) {
@@ -718,7 +721,10 @@ k_decode_main(MainArgs a) {
     int cg = -1;
     f32x16 vacc = {};
     for (int ib = i0; ib < i1; ib += 4) {
-      if (ib != i0) load_expand(a, eb, ib, i1, kind, ncol, m, h);
+      if (ib != i0) {
+        fetch_desc(a, ed, ib, i1);
+        load_operands(a, ed, eb, ib, i1, kind, ncol, m, h);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (ib + q >= i1) continue;
@@ -758,12 +764,13 @@ k_decode_main(MainArgs a) {
   // (d) row pass 2: this slice's tile = T + (V (.) e) + b (b on slice 0 only)
   f32x4 out[2 * MGT];
   {
-    f32x4 e4[2 * MGT], b4[2 * MGT];
+    if constexpr (!early) {
 #pragma unroll
-    for (int j = 0; j < 2 * MGT; ++j) {
-      const int r = rr + 16 * min(j, nj - 1);
-      e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
-      b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
+      for (int j = 0; j < 2 * MGT; ++j) {
+        const int r = rr + 16 * min(j, nj - 1);
+        e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
+        b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 2 * MGT; ++j) {
@@ -838,56 +845,47 @@ static void launch_main(const MainArgs& a, int grid, hipStream_t st) {
 scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                            float* y, hipStream_t st, int32_t* launches) {
   const DecodePlan& D = B->dp;
+  // the shrink sums of this forward and the buffer cleared for the next
+  float* acc = D.acc32[D.fwd & 1];
+  float* acc_next = D.acc32[(D.fwd + 1) & 1];
+  ++D.fwd;
   int nl = 0;
-  if (D.n_pro > 0) {
+  {
     ProArgs pa{};
     pa.x = (const uint16_t*)x;
     pa.items = D.pro_items;
     pa.n_items = D.n_pro;
     pa.vrows = D.vrows;
     pa.A_sh = (const uint16_t*)L->A_sh;
-    pa.tb = D.tb;
+    pa.xs = D.xs;
+    pa.acc = acc;
+    pa.acc_next = acc_next;
+    pa.acc_words = D.acc_bytes / 4;
+    pa.M_pad = D.M_pad;
+    pa.AW = D.AW;
     pa.RT = D.RT;
-    pa.ub = D.ub;
-    pa.r_v = L->r_v;
-    pa.delta = D.delta;
-    pa.spart = D.spart;
-    pa.scnt = D.scnt;
-    pa.spart_bytes = D.spart_bytes;
-    pa.n_sgroups = D.n_sgroups;
-    pa.KQ = D.KQ;
-    pa.vpart = D.vpart;
-    pa.vcnt = D.vcnt;
-    pa.vpart_bytes = D.vpart_bytes;
-    pa.nvb = D.nvb;
-    pa.njb = D.njb;
-    pa.SV = D.SV;
     pa.d_in = (int32_t)L->d_in;
-    const int grid = std::max(1, std::min(2048, (pa.n_items + 3) / 4));
+    const int grid = std::max(1, std::min(8192, pa.n_items));
     ProfScope ps(L, st, "decode_prologue");
-    hipLaunchKernelGGL(k_decode_prologue, dim3(grid), dim3(256), 0, st, pa);
+    hipLaunchKernelGGL(k_decode_prologue, dim3(grid), dim3(64), 0, st, pa);
     ++nl;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch k_decode_prologue");
   }
   MainArgs ma{};
-  ma.x = (const uint16_t*)x;
+  ma.xs = D.xs;
   ma.W = (const uint16_t*)W;
-  ma.delta = D.delta;
-  ma.row_tok = D.row_tok;
   ma.rows = D.rows;
   ma.items = D.exp_items;
   ma.item_ptr = D.exp_ptr;
-  ma.item_off = D.exp_off;
-  ma.tb = D.tb;
-  ma.ub = D.ub;
+  ma.acc = acc;
   ma.zeros = D.zeros;
   ma.part = D.part;
   ma.cnt = D.cnt;
   ma.y = y;
-  ma.tb_bytes = D.tb_bytes;
-  ma.ub_bytes = D.ub_bytes;
+  ma.acc_bytes = D.acc_bytes;
   ma.part_bytes = D.part_bytes;
+  for (int i = 0; i < 9; ++i) ma.off[i] = D.exp_off[i];
   ma.g_rot = D.g_rot;
   ma.d_in = (int32_t)L->d_in;
   ma.d_out = (int32_t)L->d_out;
@@ -895,7 +893,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.S = D.S;
   ma.C = D.C;
   ma.RT = D.RT;
-  ma.r_v = L->r_v;
+  ma.AW = D.AW;
   const int grid = D.C * D.S;
   ProfScope ps(L, st, "decode_main");
   switch (D.MG + D.g_rot) {

@@ -277,7 +277,7 @@ static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x,
 int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
   (void)L;
   if (B->n == 0) return 0;
-  if (B->dp.enabled) return 1 + (B->dp.n_pro > 0 ? 1 : 0);
+  if (B->dp.enabled) return 2;  // prologue (gather, rotation, shrinks) + main
   return (B->n_rot > 0) + (B->max_rank > 0) + (B->n_vera > 0) + 1 +
          (B->max_rank > 0 || B->n_vera > 0);
 }

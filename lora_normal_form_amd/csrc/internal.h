@@ -93,11 +93,11 @@ struct DecRow {
 
 // Prologue work item (one per wave), pointers and tokens resolved at plan
 // time. 48 bytes.
-//   rotation:    p0 = first sorted row, n = rows (<= 4), k = first of 64
-//                columns, tok = the rows' tokens, ptr = (R - I)^T blocks,
-//                blk = block size
+//   gather:      p0 = sorted row, tok[0] = its token
+//   rotation:    p0, n, tok as above, k = first of 64 columns,
+//                ptr = (R - I)^T blocks, blk = block size
 //   own shrink:  p0, n, tok as above, k = first rank | ranks (<= 4) << 16,
-//                ptr = A', blk = K part (1024 wide), grp = shrink group
+//                ptr = A', blk = K part (1024 wide)
 //   VeRA shrink: p0 = block of 32 VeRA rows, n = block of 32 ranks,
 //                k = K slice (512 wide)
 struct DecProItem {
@@ -118,34 +118,30 @@ struct DecVeraRow {
 struct DecodePlan {
   bool enabled = false;
   int32_t MG = 0;       // row groups of 32 covering the n sorted rows
-  int32_t g_rot = 0;    // leading row groups that hold rotated rows
+  int32_t g_rot = 0;    // row groups of delta rows (rotated rows first)
   int32_t M_pad = 0;    // 32 * MG
-  int32_t RT = 0;       // row stride of tb (max own rank rounded up to 16)
+  int32_t RT = 0;       // own-term ranks per row in the shrink buffer (max rank, to 16)
+  int32_t AW = 0;       // shrink buffer row: RT own ranks, then r_v VeRA ranks
   int32_t S = 1;        // K slices of the base GEMM (1, 2 or 4)
   int32_t C = 0;        // column tiles of 64 outputs
   int32_t k_chunk = 0;  // d_in / S
   int32_t n_pro = 0;    // prologue work items
-  int32_t nvb = 0, njb = 0, SV = 0;  // VeRA shrink blocking (K slices of 512)
-  int32_t n_sgroups = 0, KQ = 0;     // own-term shrink groups, K parts of 1024
   int32_t n_exp = 0;
-  const int32_t* row_tok = nullptr;      // [M_pad] token staged for the row (-1 past n)
+  int32_t exp_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};  // [2 S + 1] expand items by slice and kind
   const DecRow* rows = nullptr;          // [M_pad]
   const DecProItem* pro_items = nullptr; // [n_pro]
   const DecVeraRow* vrows = nullptr;     // [32 nvb]
   const int4* exp_items = nullptr;       // expand items by slice, own then VeRA
   const uint16_t* const* exp_ptr = nullptr;  // per expand item: B' or B_sh
-  const int32_t* exp_off = nullptr;      // [2 S + 1]
   const float* zeros = nullptr;          // [d_out] of 0.0f
-  uint16_t* tb = nullptr;     // [M_pad][RT] bf16 own-term shrink
-  uint16_t* ub = nullptr;     // [M_pad][r_v] bf16 VeRA shrink (times d)
-  uint16_t* delta = nullptr;  // [32 g_rot][d_in] bf16 x (R - I)
-  float* vpart = nullptr;     // [SV][nvb * njb][16][64] VeRA shrink partials
-  int32_t* vcnt = nullptr;    // [nvb * njb] arrival counters (kept at zero)
-  float* spart = nullptr;     // [KQ][n_sgroups][16] own-shrink partials
-  int32_t* scnt = nullptr;    // [n_sgroups] arrival counters (kept at zero)
+  uint16_t* xs = nullptr;     // [M_pad + 32 g_rot][d_in] bf16: sorted x rows, then delta rows
+  float* acc32[2] = {nullptr, nullptr};  // per parity: [M_pad][AW] fp32 shrink sums
   float* part = nullptr;      // [S][C][M_pad][64] split-K partial tiles (S > 1)
   int32_t* cnt = nullptr;     // [C] arrival counters (kept at zero)
-  uint32_t tb_bytes = 0, ub_bytes = 0, vpart_bytes = 0, spart_bytes = 0, part_bytes = 0;
+  uint32_t acc_bytes = 0, part_bytes = 0;
+  // forwards launched with this plan; the shrink sums alternate between the
+  // two acc32 buffers, and each forward's prologue clears the other one
+  mutable uint32_t fwd = 0;
 };
 
 }  // namespace scute

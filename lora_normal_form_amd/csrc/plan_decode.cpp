@@ -13,9 +13,9 @@
 //   VeRA item  (row group g, 64 ranks) against the shared B_sh
 // Each K slice of a tile takes a share of both kinds; own items run on the
 // tile's first two waves, VeRA items on the other two.
-// The prologue items (rotation, own-term shrink, VeRA shrink) are listed
-// here too, with every pointer and token resolved; see decode.hip for the
-// kernels.
+// The prologue items (gather of the sorted x rows, rotation, own-term
+// shrink, VeRA shrink) are listed here too, with every pointer and token
+// resolved; see decode.hip for the kernels.
 
 #include <string.h>
 
@@ -27,7 +27,7 @@ namespace scute {
 
 namespace {
 
-enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2 };
+enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3 };
 enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
 
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -83,21 +83,22 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   D.k_chunk = (int32_t)(d_in / S);
 
   // ---- counts that size the tables ------------------------------------------
-  int32_t n_rot_items = 0, n_sgroups = 0;
+  int32_t n_rot_items = 0, n_sgroups = 0, nvb = 0, njb = 0, SV = 0;
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
     if (E.flags & F_R) n_rot_items += (len + 3) / 4 * (int32_t)(d_in / 64);
     if (E.flags & F_TERM) n_sgroups += (len + 3) / 4 * ((E.rank + 3) / 4);
   }
-  D.KQ = (int32_t)((d_in + 1023) / 1024);
-  D.n_sgroups = n_sgroups;
+  const int32_t KQ = (int32_t)((d_in + 1023) / 1024);
   if (B->n_vera > 0) {
-    D.nvb = (B->n_vera + 31) / 32;
-    D.njb = L->r_v / 32;
-    D.SV = (int32_t)(d_in / 512);
+    nvb = (B->n_vera + 31) / 32;
+    njb = L->r_v / 32;
+    SV = (int32_t)(d_in / 512);
   }
-  const int32_t n_pro = n_rot_items + D.KQ * n_sgroups + D.SV * D.nvb * D.njb;
+  const int32_t n_gather = n;
+  const int32_t n_pro = n_gather + n_rot_items + KQ * n_sgroups + SV * nvb * njb;
+  D.AW = D.RT + (B->n_vera > 0 ? L->r_v : 0);
 
   // ---- expand items ----------------------------------------------------------
   // item: (type | row group << 8, first rank, 16-rank steps (<= 4) | B row
@@ -161,20 +162,19 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const auto own_per = spread(own_items, false), vera_per = spread(vera_items, true);
   std::vector<int4> exp;
   std::vector<const uint16_t*> exp_ptr;
-  std::vector<int32_t> exp_off(2 * S + 1, 0);
   for (int32_t k = 0; k < S; ++k) {
-    exp_off[2 * k] = (int32_t)exp.size();
+    D.exp_off[2 * k] = (int32_t)exp.size();
     for (const Item& it : own_per[k]) {
       exp.push_back(it.v);
       exp_ptr.push_back(it.ptr);
     }
-    exp_off[2 * k + 1] = (int32_t)exp.size();
+    D.exp_off[2 * k + 1] = (int32_t)exp.size();
     for (const Item& it : vera_per[k]) {
       exp.push_back(it.v);
       exp_ptr.push_back(it.ptr);
     }
   }
-  exp_off[2 * S] = (int32_t)exp.size();
+  D.exp_off[2 * S] = (int32_t)exp.size();
   D.n_exp = (int32_t)exp.size();
 
   // ---- one device allocation: tables, then zeroed workspaces -------------------
@@ -184,29 +184,23 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     o += al256(bytes);
     return r;
   };
-  const size_t o_tok = take(4 * (size_t)D.M_pad);
   const size_t o_rows = take(sizeof(DecRow) * (size_t)D.M_pad);
   const size_t o_pro = take(sizeof(DecProItem) * (size_t)n_pro + 16);
-  const size_t o_vrows = take(sizeof(DecVeraRow) * 32 * (size_t)D.nvb + 16);
+  const size_t o_vrows = take(sizeof(DecVeraRow) * 32 * (size_t)nvb + 16);
   const size_t o_exp = take(16 * exp.size() + 16);
   const size_t o_ptr = take(8 * exp_ptr.size() + 8);
-  const size_t o_off = take(4 * exp_off.size());
   const size_t o_ones = take(4 * (size_t)d_out);
   const size_t tables = o;
   const size_t o_zeros = take(4 * (size_t)d_out);
-  const size_t tb_bytes = 2 * (size_t)D.M_pad * D.RT;
-  const size_t ub_bytes = B->n_vera ? 2 * (size_t)D.M_pad * L->r_v : 0;
-  const size_t vpart_bytes = 4 * (size_t)D.SV * D.nvb * D.njb * 1024;
-  const size_t spart_bytes = 4 * (size_t)D.KQ * n_sgroups * 16;
+  const size_t acc_bytes = 4 * (size_t)D.M_pad * D.AW;
   const size_t part_bytes = S > 1 ? 4 * (size_t)S * D.C * D.M_pad * 64 : 0;
-  if (part_bytes >= ((size_t)1 << 31) || vpart_bytes >= ((size_t)1 << 31)) {
+  const size_t xs_bytes = 2 * (size_t)(D.M_pad + 32 * D.g_rot) * d_in;
+  if (part_bytes >= ((size_t)1 << 31) || acc_bytes >= ((size_t)1 << 31)) {
     D = DecodePlan{};  // buffer offsets are 32-bit
     return SCUTE_OK;
   }
-  const size_t o_tb = take(tb_bytes), o_ub = take(ub_bytes);
-  const size_t o_delta = take(2 * (size_t)32 * D.g_rot * d_in);
-  const size_t o_vpart = take(vpart_bytes), o_vcnt = take(4 * (size_t)D.nvb * D.njb);
-  const size_t o_spart = take(spart_bytes), o_scnt = take(4 * (size_t)n_sgroups);
+  const size_t o_xs = take(xs_bytes);
+  const size_t o_acc0 = take(acc_bytes), o_acc1 = take(acc_bytes);
   const size_t o_part = take(part_bytes), o_cnt = take(4 * (size_t)D.C);
   const size_t total = o;
 
@@ -217,10 +211,8 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const float* zeros = (const float*)(d + o_zeros);
 
   // ---- per-row tables ----------------------------------------------------------
-  std::vector<int32_t> row_tok(D.M_pad, -1);
   std::vector<DecRow> rows(D.M_pad, DecRow{ones, ones, zeros, -1, 0});
   for (int32_t p = 0; p < n; ++p) {
-    row_tok[p] = B->perm[p];
     rows[p].tok = B->perm[p];
     const int32_t a = B->row_adapter[p];
     if (a < 0) continue;
@@ -239,6 +231,14 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   auto toks = [&](DecProItem& it) {
     for (int32_t r = 0; r < 4; ++r) it.tok[r] = B->perm[it.p0 + std::min(r, it.n - 1)];
   };
+  for (int32_t p0 = 0; p0 < n; ++p0) {
+    DecProItem it{};
+    it.type = PRO_GATHER;
+    it.p0 = p0;
+    it.n = 1;
+    toks(it);
+    pro.push_back(it);
+  }
   std::vector<DecProItem> shrink_groups;
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
@@ -270,16 +270,16 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
           shrink_groups.push_back(it);
         }
   }
-  for (int32_t kq = 0; kq < D.KQ; ++kq)
+  for (int32_t kq = 0; kq < KQ; ++kq)
     for (DecProItem it : shrink_groups) {
       it.blk = kq;
       pro.push_back(it);
     }
   std::vector<DecVeraRow> vrows;
   if (B->n_vera > 0) {
-    for (int32_t kv = 0; kv < D.SV; ++kv)
-      for (int32_t vb = 0; vb < D.nvb; ++vb)
-        for (int32_t jb = 0; jb < D.njb; ++jb) {
+    for (int32_t kv = 0; kv < SV; ++kv)
+      for (int32_t vb = 0; vb < nvb; ++vb)
+        for (int32_t jb = 0; jb < njb; ++jb) {
           DecProItem it{};
           it.type = PRO_VSHRINK;
           it.p0 = vb;
@@ -287,7 +287,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
           it.k = kv;
           pro.push_back(it);
         }
-    vrows.resize(32 * (size_t)D.nvb);
+    vrows.resize(32 * (size_t)nvb);
     for (size_t v = 0; v < vrows.size(); ++v) {
       const bool real = v < (size_t)B->n_vera;
       const int32_t p = B->vera_pos[real ? v : 0];
@@ -296,6 +296,11 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
       vrows[v].p = real ? p : -1;
     }
   }
+  // heaviest items first: they start on separate compute units
+  std::stable_sort(pro.begin(), pro.end(), [](const DecProItem& p, const DecProItem& q) {
+    auto rank = [](int32_t t) { return t == PRO_VSHRINK ? 0 : t == PRO_SHRINK ? 1 : t == PRO_ROT ? 2 : 3; };
+    return rank(p.type) < rank(q.type);
+  });
   D.n_pro = (int32_t)pro.size();
   if (D.n_pro != n_pro) {
     (void)hipFree(B->fast_dev);
@@ -305,21 +310,19 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   }
 
   std::vector<uint8_t> h(tables, 0);
-  memcpy(h.data() + o_tok, row_tok.data(), 4 * row_tok.size());
   memcpy(h.data() + o_rows, rows.data(), sizeof(DecRow) * rows.size());
   if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), sizeof(DecProItem) * pro.size());
   if (!vrows.empty()) memcpy(h.data() + o_vrows, vrows.data(), sizeof(DecVeraRow) * vrows.size());
   if (!exp.empty()) memcpy(h.data() + o_exp, exp.data(), 16 * exp.size());
   if (!exp_ptr.empty()) memcpy(h.data() + o_ptr, exp_ptr.data(), 8 * exp_ptr.size());
-  memcpy(h.data() + o_off, exp_off.data(), 4 * exp_off.size());
   for (int64_t j = 0; j < d_out; ++j) {
     const float one = 1.0f;
     memcpy(h.data() + o_ones + 4 * j, &one, 4);
   }
 
-  // workspaces start at zero: rows of delta past n_rot, ranks of tb past each
-  // row's own rank, rows of ub without VeRA, and the arrival counters must
-  // read as zero
+  // workspaces start at zero: rows of xs past n and delta rows past n_rot
+  // (staged but never written), both shrink sum buffers, and the arrival
+  // counters
   e = hipMemsetAsync(d + tables, 0, total - tables, st);
   if (e == hipSuccess) e = hipMemcpyAsync(d, h.data(), tables, hipMemcpyHostToDevice, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -329,28 +332,20 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     D = DecodePlan{};
     return hip_fail(e, "upload decode plan");
   }
-  D.row_tok = (const int32_t*)(d + o_tok);
   D.rows = (const DecRow*)(d + o_rows);
   D.pro_items = (const DecProItem*)(d + o_pro);
   D.vrows = B->n_vera ? (const DecVeraRow*)(d + o_vrows) : nullptr;
   D.exp_items = (const int4*)(d + o_exp);
   D.exp_ptr = (const uint16_t* const*)(d + o_ptr);
-  D.exp_off = (const int32_t*)(d + o_off);
   D.zeros = zeros;
-  D.tb = D.RT ? (uint16_t*)(d + o_tb) : nullptr;
-  D.ub = B->n_vera ? (uint16_t*)(d + o_ub) : nullptr;
-  D.delta = D.g_rot ? (uint16_t*)(d + o_delta) : nullptr;
-  D.vpart = B->n_vera ? (float*)(d + o_vpart) : nullptr;
-  D.vcnt = B->n_vera ? (int32_t*)(d + o_vcnt) : nullptr;
-  D.spart = (float*)(d + o_spart);
-  D.scnt = (int32_t*)(d + o_scnt);
+  D.xs = (uint16_t*)(d + o_xs);
+  D.acc32[0] = (float*)(d + o_acc0);
+  D.acc32[1] = (float*)(d + o_acc1);
   D.part = S > 1 ? (float*)(d + o_part) : nullptr;
   D.cnt = (int32_t*)(d + o_cnt);
-  D.tb_bytes = (uint32_t)tb_bytes;
-  D.ub_bytes = (uint32_t)ub_bytes;
-  D.vpart_bytes = (uint32_t)vpart_bytes;
-  D.spart_bytes = (uint32_t)spart_bytes;
+  D.acc_bytes = (uint32_t)acc_bytes;
   D.part_bytes = (uint32_t)part_bytes;
+  D.fwd = 0;
   D.enabled = true;
   return SCUTE_OK;
 }

@@ -1,0 +1,128 @@
+"""Summaries of rocprofv3 output for the layer's kernels.
+
+    python -m lora_normal_form_amd.profsum stats <kernel_stats.csv>
+        Markdown table of per-kernel calls / average duration / share.
+
+    python -m lora_normal_form_amd.profsum traffic --fetch <counter_collection.csv>
+        --write <counter_collection.csv> --copy-mib N --workload NAME --out <json>
+        HBM bytes per dispatch of every kernel from a FETCH_SIZE run and a
+        WRITE_SIZE run. The counters report KiB per dispatch; each counter is
+        scaled by the factor that maps its reading for a plain device copy of
+        N MiB (the runtime's copy kernel, launched by bench.py --calib-copy N)
+        to the N MiB it actually read and wrote. The JSON records the SHA-256
+        of the kernel sources, and bench.py uses the figures only while the
+        sources are unchanged.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["csrc/decode.hip", "csrc/forward.hip", "csrc/prefill.hip"]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def source_sha() -> str:
+    """SHA-256 over the HIP kernel sources (those that exist)."""
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        path = os.path.join(PKG, rel)
+        if os.path.exists(path):
+            h.update(rel.encode())
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str):
+    """The library's name for one of its kernels (the name bench.py and
+    scute_profile_read use: "decode_main", "gemm", ...), or None for kernels
+    that are not the library's."""
+    base = name.split("(")[0]
+    if "scute::" not in base:
+        return None
+    base = base[base.index("scute::") + len("scute::"):].split("<")[0]
+    return base[2:] if base.startswith("k_") else base
+
+
+def stats_table(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    out = ["| kernel | calls | average (us) | share |", "|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | "
+                   f"{float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{100.0 * float(r['TotalDurationNs']) / total:.1f}% |")
+    return "\n".join(out)
+
+
+def counter_per_dispatch(path: str, counter: str):
+    """{kernel name: [value per dispatch]} for one counter (KiB)."""
+    per = defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        per[key[0]][key[1]] = per[key[0]].get(key[1], 0.0) + float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def traffic(fetch_csv: str, write_csv: str, copy_mib: float, workload: str) -> dict:
+    fetch = counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = counter_per_dispatch(write_csv, "WRITE_SIZE")
+
+    def copy_reading(per):
+        vals = [v for k, vs in per.items() if COPY_KERNEL in k for v in vs]
+        big = [v for v in vals if v > 0.5 * copy_mib * 1024]
+        if not big:
+            raise SystemExit(f"no {COPY_KERNEL} dispatch near {copy_mib} MiB in the counters")
+        return sum(big) / len(big)
+
+    copy_kib = copy_mib * 1024.0
+    f_scale = copy_kib / copy_reading(fetch)
+    w_scale = copy_kib / copy_reading(write)
+    kernels = {}
+    for name in sorted(set(fetch) | set(write)):
+        k = short_name(name)
+        if k is None:
+            continue
+        fv, wv = fetch.get(name, []), write.get(name, [])
+        kernels[k] = {
+            "dispatches": max(len(fv), len(wv)),
+            "fetch_bytes": (sum(fv) / len(fv)) * f_scale * 1024.0 if fv else None,
+            "write_bytes": (sum(wv) / len(wv)) * w_scale * 1024.0 if wv else None,
+        }
+    return {"workload": workload, "source_sha": source_sha(), "copy_mib": copy_mib,
+            "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-mib", type=float, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats_table(a.csv))
+    else:
+        res = traffic(a.fetch, a.write, a.copy_mib, a.workload)
+        with open(a.out, "w") as f:
+            json.dump(res, f, indent=1)
+        print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    sys.exit(main())
