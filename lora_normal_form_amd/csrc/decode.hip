@@ -10,7 +10,7 @@
 //               stored after the sorted x rows;
 //   own shrink  t = x A' for up to 4 rows x 4 ranks over a K part of 1024;
 //   VeRA shrink u = (x A_sh) (.) d for 32 VeRA rows x 32 ranks over a K
-//               slice of 512, on one 32x32x16 MFMA tile.
+//               slice of 256, on one 32x32x16 MFMA tile.
 // Rotation runs before the shared GEMM and the shared VeRA pair is read once
 // per step for the whole batch ("Where is the cheapest place to compute the
 // remaining slots?", paper-daily.com explainer of "Scute: Exact Batched
@@ -279,13 +279,13 @@ k_decode_prologue(ProArgs a) {
         atomicAdd(a.acc + (size_t)(item.p0 + r) * a.AW + k0 + j, mine);
     } else {
       // VeRA shrink block: 32 VeRA rows x 32 ranks of A_sh over one K slice
-      // of 512 (two rounds of loads), scaled by d (per rank, so it commutes
+      // of 256 (one round of loads), scaled by d (per rank, so it commutes
       // with the K sum) and added into the row's VeRA slots
       const int32_t vb = item.p0, jb = item.n, kv = item.k;
       const int m = lane & 31, h = lane >> 5;
       const DecVeraRow vr = a.vrows[32 * vb + m];
-      const uint16_t* xr = a.x + (size_t)vr.tok * d_in + (int64_t)kv * 512 + 32 * h;
-      const uint16_t* ar = a.A_sh + (size_t)(32 * jb + m) * d_in + (int64_t)kv * 512 + 32 * h;
+      const uint16_t* xr = a.x + (size_t)vr.tok * d_in + (int64_t)kv * 256 + 32 * h;
+      const uint16_t* ar = a.A_sh + (size_t)(32 * jb + m) * d_in + (int64_t)kv * 256 + 32 * h;
       // output element i: VeRA row 32 vb + 8 (i / 4) + 4 h + i % 4, rank 32 jb + m
       const int32_t j = 32 * jb + m;
       float dsc[16];
@@ -297,13 +297,12 @@ k_decode_prologue(ProArgs a) {
         dsc[i] = ldg(o.vd + j);
       }
       f32x16 acc = {};
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      {
         uint4 xa[16], wa[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          xa[q] = ldg16(xr + 256 * half + 64 * (q >> 2) + 8 * (q & 3));
-          wa[q] = ldg16(ar + 256 * half + 64 * (q >> 2) + 8 * (q & 3));
+          xa[q] = ldg16(xr + 64 * (q >> 2) + 8 * (q & 3));
+          wa[q] = ldg16(ar + 64 * (q >> 2) + 8 * (q & 3));
         }
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc = mfma32(xa[q], wa[q], acc);
@@ -422,30 +421,32 @@ __device__ __forceinline__ void kstep(int t, int nst, const WSrc& wrow,
   mma_stage<MGT>(cur + kp * DecCfg<MGT>::STAGE, wc, acc, m, h);
 }
 
-// The same step with the stage index T known at compile time: stages past
+// The same step with the stage index T known at compile time: W is
+// prefetched LW stages ahead into a ring of LW + 1 register sets (W is the
+// stream from HBM, so it runs further ahead than the LDS rows), stages past
 // the last are not prefetched, and the wait counts exactly the loads issued
-// after stage T's rows (R = 3: the next stage's W and rows, issued by the
-// previous step; this step's W), so no load is repeated and every wait is
-// exact. Expands to the steps T .. NST-1.
-template <int MGT, int NST, int T>
+// after stage T's rows (R = 3: the next stage's rows and W issued by the
+// previous step; this step's W). Expands to the steps T .. NST-1.
+template <int MGT, int NST, int LW, int T>
 __device__ __forceinline__ void ksteps_static(const WSrc& wrow, const uint16_t* const (&src)[2 * MGT],
                                               uint8_t* s0, uint8_t* s1, uint8_t* s2,
-                                              uint4 (&wb)[3][4], f32x16 (&acc)[MGT], int m, int h,
-                                              int cb, int kp) {
+                                              uint4 (&wb)[LW + 1][4], f32x16 (&acc)[MGT], int m,
+                                              int h, int cb, int kp) {
   if constexpr (T < NST) {
     using Cfg = DecCfg<MGT>;
     constexpr int R = Cfg::R;
-    constexpr int TN = T + R - 1;  // stage this step prefetches
-    constexpr bool pre = TN < NST;
-    constexpr int allowed = (R == 3 && T + 1 < NST ? Cfg::PER_STAGE : 0) + (pre ? 4 : 0);
+    constexpr int TN = T + R - 1;   // rows this step prefetches
+    constexpr int TW = T + LW;      // W this step prefetches
+    constexpr int allowed = (R == 3 && T + 1 < NST ? 2 * MGT : 0) +
+                            (R == 3 && T - 1 + LW < NST ? 4 : 0) + (TW < NST ? 4 : 0);
     uint8_t* cur = T % R == 0 ? s0 : (T % R == 1 ? s1 : s2);
     uint8_t* nxt = TN % R == 0 ? s0 : (TN % R == 1 ? s1 : s2);
-    if constexpr (pre) load_w(wb[TN % R], wrow, (int64_t)SK * TN);
+    if constexpr (TW < NST) load_w(wb[TW % (LW + 1)], wrow, (int64_t)SK * TW);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(allowed));
     wg_barrier();
-    if constexpr (pre) stage_rows<MGT>(nxt + kp * Cfg::STAGE, src, (int64_t)SK * TN, cb);
-    mma_stage<MGT>(cur + kp * Cfg::STAGE, wb[T % R], acc, m, h);
-    ksteps_static<MGT, NST, T + 1>(wrow, src, s0, s1, s2, wb, acc, m, h, cb, kp);
+    if constexpr (TN < NST) stage_rows<MGT>(nxt + kp * Cfg::STAGE, src, (int64_t)SK * TN, cb);
+    mma_stage<MGT>(cur + kp * Cfg::STAGE, wb[T % (LW + 1)], acc, m, h);
+    ksteps_static<MGT, NST, LW, T + 1>(wrow, src, s0, s1, s2, wb, acc, m, h, cb, kp);
   }
 }
 
@@ -561,12 +562,10 @@ k_decode_main(MainArgs a) {
   const int mgx = MGT - a.g_rot;  // x row groups
   const int Mx = 32 * mgx;
 
-  // XCD-aware tile order: work-groups are dispatched round-robin over the 8
-  // XCDs, so consecutive work indices (the S slices of one tile) land on one
-  // XCD and share its L2 for the tile's x rows
-  const int G = gridDim.x, bid = blockIdx.x;
-  const int w = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
-  const int c = w / a.S, kc = w - c * a.S;
+  // grid (tile, slice): work-groups are dispatched round-robin over the 8
+  // XCDs in linear order slice * C + tile, so with C a multiple of 8 the S
+  // slices of a tile share one XCD and its L2
+  const int c = blockIdx.x, kc = blockIdx.y;
 
   const int64_t ncol = (int64_t)c * 64 + cb * 32 + m;
   const int kw = a.k_chunk / 2;  // K per half
@@ -576,18 +575,22 @@ k_decode_main(MainArgs a) {
                   (uint32_t)(((size_t)ncol * a.d_in + kbase + 32 * h) * 2)};
 
   // (0) record of the row this thread keeps for the epilogue
-  u32x4 rec0 = {0, 0, 0, 0}, rec1 = {0, 0, 0, 0};
-  if (tid < Mx) {
-    const GLOBAL u32x4* rp = (const GLOBAL u32x4*)(a.rows + tid);
-    rec0 = rp[0];
-    rec1 = rp[1];
-  }
-  // (1) W of the first R-1 stages
-  // (with NST known, stages past the last are not loaded)
+  // (branch-free, so the compiler can fetch the kernel arguments at once)
+  const GLOBAL u32x4* rp = (const GLOBAL u32x4*)(a.rows + min(tid, Mx - 1));
+  const u32x4 rec0 = rp[0], rec1 = rp[1];
+  // (1) W of the first LW = R - 1 stages (with NST known, stages past the
+  //     last are not loaded)
+  constexpr int LW = R - 1;
   constexpr bool pre1 = R == 3 && NST != 1;
-  uint4 wb[3][4];
+  uint4 wb[LW + 1][4];
   load_w(wb[0], wrow, 0);
-  if constexpr (pre1) load_w(wb[1], wrow, (int64_t)SK * min(1, nst - 1));
+  if constexpr (NST > 0) {
+#pragma unroll
+    for (int t = 1; t < LW; ++t)
+      if (t < NST) load_w(wb[t], wrow, (int64_t)SK * t);
+  } else if constexpr (pre1) {
+    load_w(wb[1], wrow, (int64_t)SK * min(1, nst - 1));
+  }
   // (2) row sources: staged row r (x rows, then delta rows) is row r of xs
   const uint16_t* src[2 * MGT];
   {
@@ -611,6 +614,7 @@ k_decode_main(MainArgs a) {
   }
   ExpDesc ed;
   if (i0 < i1) fetch_desc(a, ed, i0, i1);
+  ExpBatch eb;
 
   f32x16 acc[MGT];
 #pragma unroll
@@ -618,12 +622,13 @@ k_decode_main(MainArgs a) {
 
   // stage 0 (peeled: the row records go to LDS after its barrier)
   {
-    constexpr bool pre = NST == 0 || R - 1 < NST;
+    constexpr bool pre = NST == 0 || R - 1 < NST;   // rows of stage R-1
+    constexpr bool prew = NST == 0 || LW < NST;     // W of stage LW
     const int64_t kn = (int64_t)SK * min(R - 1, nst - 1);
-    if constexpr (pre) load_w(wb[R - 1], wrow, kn);
+    if constexpr (prew) load_w(wb[LW], wrow, (int64_t)SK * min(LW, nst - 1));
     // issued after the rows of stage 0: (R == 3: rows of stage 1) and W of
-    // stage R-1
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((pre1 ? 2 * MGT : 0) + (pre ? 4 : 0)));
+    // stage LW
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((pre1 ? 2 * MGT : 0) + (prew ? 4 : 0)));
     wg_barrier();
     if (tid < Mx) {
       rec[tid][0] = rec0;
@@ -636,7 +641,7 @@ k_decode_main(MainArgs a) {
   // remaining stages; stage t lives in ring slot t % R and W registers
   // wb[t % R], named statically in both forms of the loop
   if constexpr (NST > 0) {
-    ksteps_static<MGT, NST, 1>(wrow, src, slot0, slot1, slot2, wb, acc, m, h, cb, kp);
+    ksteps_static<MGT, NST, LW, 1>(wrow, src, slot0, slot1, slot2, wb, acc, m, h, cb, kp);
   } else if constexpr (R == 3) {
 #pragma unroll 1
     for (int t = 1; t < nst; t += 3) {
@@ -660,18 +665,17 @@ k_decode_main(MainArgs a) {
   // ---- epilogue ---------------------------------------------------------------
   // the first expand batch's operands and the rows' factor vectors are in
   // flight while the K halves meet
-  ExpBatch eb;
   if (i0 < i1) load_operands(a, ed, eb, i0, i1, kind, ncol, m, h);
   const int q4 = tid & 15, rr = tid >> 4;  // float4 of the row, row within 16
   const int nj = 2 * mgx;                  // passes of 16 rows over the x rows
   const int64_t cbase = (int64_t)c * 64 + 4 * q4;
-  constexpr bool early = MGT <= 6;         // register room to prefetch e and b too
+  constexpr bool early_f = MGT <= 6;       // register room to fetch e and b here too
   f32x4 s4[2 * MGT], e4[2 * MGT], b4[2 * MGT];
 #pragma unroll
   for (int j = 0; j < 2 * MGT; ++j) {
     const int r = rr + 16 * min(j, nj - 1);
     s4[j] = ldg4(rec_ptr(rec[r][0], 0) + cbase);
-    if constexpr (early) {
+    if constexpr (early_f) {
       e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
       b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
     }
@@ -764,7 +768,7 @@ k_decode_main(MainArgs a) {
   // (d) row pass 2: this slice's tile = T + (V (.) e) + b (b on slice 0 only)
   f32x4 out[2 * MGT];
   {
-    if constexpr (!early) {
+    if constexpr (!early_f) {
 #pragma unroll
       for (int j = 0; j < 2 * MGT; ++j) {
         const int r = rr + 16 * min(j, nj - 1);
@@ -834,7 +838,7 @@ k_decode_main(MainArgs a) {
 // ---------------------------------------------------------------------------
 
 template <int MGT>
-static void launch_main(const MainArgs& a, int grid, hipStream_t st) {
+static void launch_main(const MainArgs& a, dim3 grid, hipStream_t st) {
   switch (a.k_chunk / 2 / SK) {
     case 8: hipLaunchKernelGGL((k_decode_main<MGT, 8>), dim3(grid), dim3(256), 0, st, a); break;
     case 32: hipLaunchKernelGGL((k_decode_main<MGT, 32>), dim3(grid), dim3(256), 0, st, a); break;
@@ -894,7 +898,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.C = D.C;
   ma.RT = D.RT;
   ma.AW = D.AW;
-  const int grid = D.C * D.S;
+  const dim3 grid(D.C, D.S);
   ProfScope ps(L, st, "decode_main");
   switch (D.MG + D.g_rot) {
     case 1: launch_main<1>(ma, grid, st); break;

@@ -99,7 +99,7 @@ struct DecRow {
 //   own shrink:  p0, n, tok as above, k = first rank | ranks (<= 4) << 16,
 //                ptr = A', blk = K part (1024 wide)
 //   VeRA shrink: p0 = block of 32 VeRA rows, n = block of 32 ranks,
-//                k = K slice (512 wide)
+//                k = K slice (256 wide)
 struct DecProItem {
   int32_t type, p0, n, k;
   int32_t tok[4];

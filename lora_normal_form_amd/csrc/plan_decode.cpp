@@ -50,7 +50,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   if (d_in % 128 != 0 || d_in > 8192 || d_out % 64 != 0) return SCUTE_OK;
   // W is addressed through a buffer range with 32-bit offsets
   if (d_in * d_out * 2 >= ((int64_t)1 << 32)) return SCUTE_OK;
-  if (B->n_vera > 0 && (L->r_v % 32 != 0 || d_in % 512 != 0)) return SCUTE_OK;
+  if (B->n_vera > 0 && (L->r_v % 32 != 0 || d_in % 256 != 0)) return SCUTE_OK;
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const SlotEntry& E = L->table[B->seg[3 * i]];
     if ((E.flags & F_TERM) && (E.rank % 8 != 0)) return SCUTE_OK;
@@ -94,7 +94,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   if (B->n_vera > 0) {
     nvb = (B->n_vera + 31) / 32;
     njb = L->r_v / 32;
-    SV = (int32_t)(d_in / 512);
+    SV = (int32_t)(d_in / 256);
   }
   const int32_t n_gather = n;
   const int32_t n_pro = n_gather + n_rot_items + KQ * n_sgroups + SV * nvb * njb;
