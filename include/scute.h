@@ -239,7 +239,7 @@ typedef struct scute_batch_info {
   int32_t n_rot_rows;  /* rows 0 .. n_rot_rows-1 of the sorted order rotate */
   int32_t n_vera_rows;
   int32_t max_rank;
-  int32_t path;        /* kernels the forward will run: 0 generic, 1 MFMA decode */
+  int32_t path;        /* kernels the forward will run: 0 generic, 1 MFMA decode, 2 MFMA prefill */
 } scute_batch_info;
 
 scute_status scute_batch_info_get(const scute_batch* batch, scute_batch_info* out);

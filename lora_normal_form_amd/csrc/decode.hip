@@ -38,119 +38,15 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "kernels.h"
 
 namespace scute {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-namespace {
-
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-__device__ __forceinline__ uint16_t f2bf(float v) {
-  uint32_t u = __float_as_uint(v);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ bf16x8 as_frag(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
-__device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(a), as_frag(b), c, 0, 0, 0);
-}
-// Pointers read from tables are generic to the compiler; loads through these
-// helpers name the global address space so they become global (not flat)
-// loads and need no wait on the LDS counter.
-#define GLOBAL __attribute__((address_space(1)))
-template <typename T>
-__device__ __forceinline__ T ldg(const T* p) {
-  return *(const GLOBAL T*)p;
-}
-__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
-  const u32x4 v = *(const GLOBAL u32x4*)p;
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ f32x4 ldg4(const float* p) { return *(const GLOBAL f32x4*)p; }
-__device__ __forceinline__ void stg4(float* p, f32x4 v) { *(GLOBAL f32x4*)p = v; }
-__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
-  const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s += __uint_as_float(av[i] << 16) * __uint_as_float(bv[i] << 16);
-    s += __uint_as_float(av[i] & 0xFFFF0000u) * __uint_as_float(bv[i] & 0xFFFF0000u);
-  }
-  return s;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-// Raw buffer resources over a byte range: loads past the range return zero,
-// stores past it are dropped. (The third word's data-format field must be
-// non-zero on gfx9 for raw dword accesses.)
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ldb16(rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-// Exchange of partial results between work-groups on any XCD without
-// whole-cache maintenance: the exchanged values are written and read with
-// system-coherent buffer accesses (cache policy sc0 sc1: written through to
-// memory, read from memory, past the per-XCD L2). They are ordinary
-// compiler-visible memory operations, so the compiler waits for their
-// results. A writer waits for its stores to complete before announcing them
-// with an atomic on a counter; a reader issues its loads only after the
-// atomic that saw every announcement has returned.
-constexpr int CPOL_SYS = 17;  // sc0 | sc1
-__device__ __forceinline__ void st_sys(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CPOL_SYS);
-}
-__device__ __forceinline__ float ld_sys(rsrc_t r, uint32_t off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_SYS));
-}
-__device__ __forceinline__ void st_sys4(rsrc_t r, uint32_t off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL_SYS);
-}
-__device__ __forceinline__ f32x4 ld_sys4(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_SYS));
-}
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ int arrive(int32_t* cnt) {
-  return __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-__device__ __forceinline__ void reset_counter(int32_t* cnt) {
-  __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-}
-
-enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3 };
-enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
-
-}  // namespace
 
 // ---------------------------------------------------------------------------
 // prologue
 // ---------------------------------------------------------------------------
-
-struct ProArgs {
-  const uint16_t* x;
-  const DecProItem* items;
-  int32_t n_items;
-  const DecVeraRow* vrows;  // [32 nvb]
-  const uint16_t* A_sh;     // [r_v][d_in]
-  uint16_t* xs;             // [M_pad + 32 g_rot][d_in] sorted x rows, then delta rows
-  float* acc;               // [M_pad][AW] this forward's shrink sums (zero on entry)
-  float* acc_next;          // the other buffer, cleared for the next forward
-  uint32_t acc_words;       // M_pad * AW (a multiple of 4)
-  int32_t M_pad, AW, RT;
-  int32_t d_in;
-};
 
 // delta rows for one rotated item (<= 4 rows, one 64-column chunk): lane
 // handles output column col of block kb = col / blk; the block's (R - I)^T
@@ -175,6 +71,24 @@ __device__ __forceinline__ void rotate_rows(const uint16_t* Pt, int32_t blk,
 #pragma unroll
       for (int q = 0; q < CH / 8; ++q) acc[r] += dot8(xv[r][q], pv[q]);
   }
+}
+
+// One 32x32 shrink tile over a K slice of 256 on 32x32x16 MFMA: lane (m, h)
+// holds row m of both operands (xr: its x row, ar: its A row, each already
+// offset to the slice and to the lane's 32-element half of every 64-element
+// block; the k order inside a block is permuted identically on both).
+// Element i of the result: operand-a row 8 (i / 4) + 4 h + i % 4, A row m.
+__device__ __forceinline__ f32x16 shrink_tile(const uint16_t* xr, const uint16_t* ar) {
+  uint4 xa[16], wa[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    xa[q] = ldg16(xr + 64 * (q >> 2) + 8 * (q & 3));
+    wa[q] = ldg16(ar + 64 * (q >> 2) + 8 * (q & 3));
+  }
+  f32x16 acc = {};
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc = mfma32(xa[q], wa[q], acc);
+  return acc;
 }
 
 // One wave per work-group, so consecutive items (the heavy VeRA-shrink items
@@ -277,7 +191,7 @@ k_decode_prologue(ProArgs a) {
       const int r = lane >> 2, j = lane & 3;
       if (lane < 16 && r < len && j < nk)
         atomicAdd(a.acc + (size_t)(item.p0 + r) * a.AW + k0 + j, mine);
-    } else {
+    } else if (item.type == PRO_VSHRINK) {
       // VeRA shrink block: 32 VeRA rows x 32 ranks of A_sh over one K slice
       // of 256 (one round of loads), scaled by d (per rank, so it commutes
       // with the K sum) and added into the row's VeRA slots
@@ -296,20 +210,25 @@ k_decode_prologue(ProArgs a) {
         prow[i] = o.p;
         dsc[i] = ldg(o.vd + j);
       }
-      f32x16 acc = {};
-      {
-        uint4 xa[16], wa[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          xa[q] = ldg16(xr + 64 * (q >> 2) + 8 * (q & 3));
-          wa[q] = ldg16(ar + 64 * (q >> 2) + 8 * (q & 3));
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc = mfma32(xa[q], wa[q], acc);
-      }
+      const f32x16 acc = shrink_tile(xr, ar);
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + a.RT + j, acc[i] * dsc[i]);
+    } else if (item.type == PRO_OSHRINK) {
+      // own-term shrink on MFMA (long segments): 32 sorted rows of one adapter
+      // x 32 ranks of its A' over one K slice of 256; lanes past the rows or
+      // ranks repeat the last one and their sums are not stored
+      const int32_t p0 = item.p0, nr = item.n, k0 = item.k & 0xFFFF, nk = item.k >> 16;
+      const int m = lane & 31, h = lane >> 5;
+      const int64_t koff = (int64_t)item.blk * 256 + 32 * h;
+      const int32_t tok = ldg(a.perm + p0 + min(m, nr - 1));
+      const f32x16 acc = shrink_tile(a.x + (size_t)tok * d_in + koff,
+                                     item.ptr + (size_t)(k0 + min(m, nk - 1)) * d_in + koff);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * h + (i & 3);
+        if (row < nr && m < nk) atomicAdd(a.acc + (size_t)(p0 + row) * a.AW + k0 + m, acc[i]);
+      }
     }
   }
 }
@@ -350,14 +269,7 @@ struct DecCfg {
   static constexpr int WAIT = (R - 2) * PER_STAGE + 4;
 };
 
-// s_waitcnt immediate (gfx9 encoding) waiting until at most `n` vector
-// memory operations are outstanding; export and LDS counters unconstrained
-constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// Work-group barrier that orders LDS traffic without waiting for outstanding
-// global loads (the LDS-filling loads are awaited explicitly with s_waitcnt
-// before it; LDS reads are consumed before it in program order).
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Staged rows: 32 MGT rows (x rows of the sorted batch, then delta rows) of
 // SROW bytes; the 16-byte piece index is XOR-swizzled by (row >> 1) & 7 to
@@ -465,15 +377,6 @@ struct ExpBatch {
   int32_t gi[4];
 };
 
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ const uint16_t* uni_ptr(const uint16_t* p) {
-  const uint64_t v = (uint64_t)p;
-  return (const uint16_t*)(((uint64_t)(uint32_t)uni((int)(v >> 32)) << 32) |
-                           (uint32_t)uni((int)(uint32_t)v));
-}
-__device__ __forceinline__ uint32_t pack_bf2(uint32_t lo, uint32_t hi) {
-  return (uint32_t)f2bf(__uint_as_float(lo)) | ((uint32_t)f2bf(__uint_as_float(hi)) << 16);
-}
 
 __device__ __forceinline__ void fetch_desc(const MainArgs& a, ExpDesc& d, int ib, int i1) {
 #pragma unroll
@@ -837,6 +740,10 @@ k_decode_main(MainArgs a) {
 // launcher
 // ---------------------------------------------------------------------------
 
+void launch_prologue(const ProArgs& pa, int grid, hipStream_t st) {
+  hipLaunchKernelGGL(k_decode_prologue, dim3(grid), dim3(64), 0, st, pa);
+}
+
 template <int MGT>
 static void launch_main(const MainArgs& a, dim3 grid, hipStream_t st) {
   switch (a.k_chunk / 2 / SK) {
@@ -857,6 +764,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   {
     ProArgs pa{};
     pa.x = (const uint16_t*)x;
+    pa.perm = B->d_perm;
     pa.items = D.pro_items;
     pa.n_items = D.n_pro;
     pa.vrows = D.vrows;
@@ -871,7 +779,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
     pa.d_in = (int32_t)L->d_in;
     const int grid = std::max(1, std::min(8192, pa.n_items));
     ProfScope ps(L, st, "decode_prologue");
-    hipLaunchKernelGGL(k_decode_prologue, dim3(grid), dim3(64), 0, st, pa);
+    launch_prologue(pa, grid, st);
     ++nl;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch k_decode_prologue");

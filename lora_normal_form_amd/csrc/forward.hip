@@ -278,6 +278,7 @@ int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
   (void)L;
   if (B->n == 0) return 0;
   if (B->dp.enabled) return 2;  // prologue (gather, rotation, shrinks) + main
+  if (B->pp.enabled) return (B->pp.n_pro > 0) + 1;  // prologue (rotation, shrinks) + main
   return (B->n_rot > 0) + (B->max_rank > 0) + (B->n_vera > 0) + 1 +
          (B->max_rank > 0 || B->n_vera > 0);
 }
@@ -285,6 +286,7 @@ int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
 scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                             float* y, hipStream_t st, int32_t* launches) {
   if (B->dp.enabled) return launch_decode(L, B, x, W, y, st, launches);
+  if (B->pp.enabled) return launch_prefill(L, B, x, W, y, st, launches);
   if (L->act == SCUTE_BF16)
     return launch_ref<uint16_t>(L, B, (const uint16_t*)x, (const uint16_t*)W, y, st, launches);
   return launch_ref<float>(L, B, (const float*)x, (const float*)W, y, st, launches);

@@ -100,6 +100,12 @@ struct DecRow {
 //                ptr = A', blk = K part (1024 wide)
 //   VeRA shrink: p0 = block of 32 VeRA rows, n = block of 32 ranks,
 //                k = K slice (256 wide)
+//   own shrink on MFMA (prefill): p0 = first of up to 32 sorted rows of one
+//                adapter, n = rows, k = first rank | ranks (<= 32) << 16,
+//                ptr = A', blk = K slice (256 wide)
+enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3, PRO_OSHRINK = 4 };
+// expand item kinds of the decode main kernel
+enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
 struct DecProItem {
   int32_t type, p0, n, k;
   int32_t tok[4];
@@ -144,6 +150,42 @@ struct DecodePlan {
   mutable uint32_t fwd = 0;
 };
 
+// Chunk of a prefill batch: the rows of one adapter segment (or of rows
+// without an adapter) that one row tile of the prefill GEMM covers: up to 128
+// tokens, or up to 64 tokens followed by their 64 Delta rows when the adapter
+// rotates (the Delta rows fold into the token rows in registers); always 128
+// staged rows. Every live slot is uniform over the chunk; absent factor
+// vectors point at shared ones (s, e) and zeros (b). 64 bytes.
+struct PfChunk {
+  int32_t x0;          // sorted position of the chunk's first token
+  int32_t nx;          // tokens in the chunk
+  int32_t rows;        // token rows held by the tile (128, or 64 with rotation)
+  int32_t flags;       // PF_* below
+  const float* s;      // live s, or ones
+  const float* e;      // VeRA e, or ones
+  const float* b;      // shift b, or zeros
+  const uint16_t* Bp;  // own B' [d_out][rank], or null
+  int32_t rank;        // own rank (0 without an own term)
+  int32_t pad[3];
+};
+enum : int32_t { PF_OWN = 1, PF_VERA = 2, PF_ROT = 4 };
+
+struct PrefillPlan {
+  bool enabled = false;
+  int32_t n_chunks = 0;
+  int32_t C = 0;        // column tiles of 256 outputs
+  int32_t RT = 0;       // own-term ranks per row in the shrink buffer (max rank, to 16)
+  int32_t AW = 0;       // shrink buffer row: RT own ranks, then r_v VeRA ranks
+  int32_t n_pro = 0;    // prologue work items
+  const PfChunk* chunks = nullptr;        // [n_chunks]
+  const int32_t* crow = nullptr;          // [n_chunks][128] staged row sources
+  const DecProItem* pro_items = nullptr;  // rotation, shrinks
+  const DecVeraRow* vrows = nullptr;      // [32 nvb]
+  float* acc32[2] = {nullptr, nullptr};   // per parity: [n][AW] fp32 shrink sums
+  uint32_t acc_bytes = 0;
+  mutable uint32_t fwd = 0;
+};
+
 }  // namespace scute
 
 struct scute_batch {
@@ -171,6 +213,8 @@ struct scute_batch {
   float* u = nullptr;         // [n][r_v] VeRA shrink scaled by d (rows with VeRA)
   void* fast_dev = nullptr;   // decode-path tables + workspaces (one allocation)
   scute::DecodePlan dp;
+  void* pf_dev = nullptr;     // prefill-path tables + workspaces (one allocation)
+  scute::PrefillPlan pp;
   int32_t nseg() const { return (int32_t)(seg.size() / 3); }
 };
 
@@ -197,6 +241,29 @@ int32_t forward_launch_count(const scute_layer* L, const scute_batch* B);
 scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t st);
 scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                            float* y, hipStream_t st, int32_t* launches);
+
+// prefill path (prefill.hip / plan_prefill.cpp)
+scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_t st);
+scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x, const void* W,
+                            float* y, hipStream_t st, int32_t* launches);
+
+// Arguments of the prologue kernel (decode.hip), shared by the decode and
+// prefill paths.
+struct ProArgs {
+  const uint16_t* x;
+  const int32_t* perm;      // sorted position -> token (own-term MFMA shrink items)
+  const DecProItem* items;
+  int32_t n_items;
+  const DecVeraRow* vrows;  // [32 nvb]
+  const uint16_t* A_sh;     // [r_v][d_in]
+  uint16_t* xs;             // [M_pad + 32 g_rot][d_in] sorted x rows, then delta rows
+  float* acc;               // [M_pad][AW] this forward's shrink sums (zero on entry)
+  float* acc_next;          // the other buffer, cleared for the next forward
+  uint32_t acc_words;       // M_pad * AW (a multiple of 4)
+  int32_t M_pad, AW, RT;
+  int32_t d_in;
+};
+void launch_prologue(const ProArgs& pa, int grid, hipStream_t st);
 
 // Kernel timing: when the layer has profiling on, bracket each launch with a
 // HIP event pair on the launch stream.

@@ -40,9 +40,10 @@ void free_batch_memory(scute_batch* B) {
     if (B->dev) (void)hipFree(B->dev);
     if (B->ws) (void)hipFree(B->ws);
     if (B->fast_dev) (void)hipFree(B->fast_dev);
+    if (B->pf_dev) (void)hipFree(B->pf_dev);
     if (prev != dev && prev >= 0) (void)hipSetDevice(prev);
   }
-  B->dev = B->ws = B->fast_dev = nullptr;
+  B->dev = B->ws = B->fast_dev = B->pf_dev = nullptr;
 }
 
 }  // namespace
@@ -153,6 +154,7 @@ extern "C" scute_status scute_plan_batch(scute_layer* L, const int32_t* token_ad
         return hip_fail(e, "plan upload / workspace");
       }
       scute_status ds = build_decode_plan(L, B, s);
+      if (ds == SCUTE_OK && !B->dp.enabled) ds = build_prefill_plan(L, B, s);
       restore();
       if (ds != SCUTE_OK) {
         free_batch_memory(B);
@@ -183,7 +185,7 @@ extern "C" scute_status scute_batch_info_get(const scute_batch* B, scute_batch_i
   out->n_rot_rows = B->n_rot;
   out->n_vera_rows = B->n_vera;
   out->max_rank = B->max_rank;
-  out->path = B->dp.enabled ? 1 : 0;
+  out->path = B->dp.enabled ? 1 : (B->pp.enabled ? 2 : 0);
   return SCUTE_OK;
 }
 

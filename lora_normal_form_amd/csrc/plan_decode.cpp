@@ -27,9 +27,6 @@ namespace scute {
 
 namespace {
 
-enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3 };
-enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
-
 size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 int env_int(const char* name, int dflt) {

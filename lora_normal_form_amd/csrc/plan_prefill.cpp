@@ -1,0 +1,234 @@
+// Tables of the MFMA prefill path (bf16, long adapter segments).
+//
+// The base GEMM y = (x W + delta W) (.) s + b runs on tiles of 128 staged
+// rows by 256 output columns over the whole K dimension. The rows of a tile
+// come from one adapter segment ("Where is the cheapest place to compute the
+// remaining slots?", paper-daily.com explainer of "Scute: Exact Batched
+// Serving for PEFT Adapters Beyond LoRA": tiles belong to one adapter), so
+// the tile's epilogue applies one s, b, e and one own B' to every row: a
+// chunk is up to 128 tokens of a segment, or up to 64 tokens and their 64
+// Delta rows when the adapter rotates. The expand runs in the same epilogue
+// as extra MFMA steps whose A operand is the chunk's shrink sums.
+// The prologue (rotation Delta = x (R - I), own-term and VeRA shrinks) uses
+// the decode path's prologue kernel with MFMA shrink items.
+
+#include <string.h>
+
+#include <algorithm>
+
+#include "internal.h"
+
+namespace scute {
+
+namespace {
+
+size_t al256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = getenv(name);
+  return (v && *v) ? atoi(v) : dflt;
+}
+
+}  // namespace
+
+scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_t st) {
+  PrefillPlan& P = B->pp;
+  P = PrefillPlan{};
+  const int32_t n = B->n;
+  const int64_t d_in = L->d_in, d_out = L->d_out;
+  if (env_int("SCUTE_PREFILL", 1) == 0) return SCUTE_OK;
+  if (L->act != SCUTE_BF16 || n <= 0) return SCUTE_OK;
+  // the main kernel's K loop is unrolled for 64 stages of 64
+  if (d_in != 4096 || d_out % 256 != 0) return SCUTE_OK;
+  if (d_in * d_out * 2 >= ((int64_t)1 << 32)) return SCUTE_OK;
+  if (B->n_rot > 0 && !B->delta) return SCUTE_OK;
+  if (B->n_vera > 0 && L->r_v % 64 != 0) return SCUTE_OK;
+  for (int32_t i = 0; i < B->nseg(); ++i) {
+    const SlotEntry& E = L->table[B->seg[3 * i]];
+    if ((E.flags & F_TERM) && (E.rank % 8 != 0)) return SCUTE_OK;
+  }
+
+  P.RT = (B->max_rank + 15) / 16 * 16;
+  P.AW = P.RT + (B->n_vera > 0 ? L->r_v : 0);
+  P.C = (int32_t)(d_out / 256);
+
+  // ---- chunks ---------------------------------------------------------------
+  // segments cover the adapted rows [0, n_adapted); the rows without an
+  // adapter follow them
+  std::vector<int32_t> segs(B->seg);
+  int32_t n_adapted = 0;
+  for (int32_t i = 0; i < B->nseg(); ++i) n_adapted = std::max(n_adapted, segs[3 * i + 1] + segs[3 * i + 2]);
+  if (n_adapted < n) {
+    segs.push_back(-1);
+    segs.push_back(n_adapted);
+    segs.push_back(n - n_adapted);
+  }
+  std::vector<PfChunk> chunks;
+  std::vector<int32_t> crow;
+  for (size_t i = 0; i < segs.size() / 3; ++i) {
+    const int32_t a = segs[3 * i], start = segs[3 * i + 1], len = segs[3 * i + 2];
+    const SlotEntry* E = a >= 0 ? &L->table[a] : nullptr;
+    const bool rot = E && (E->flags & F_R);
+    const int32_t step = rot ? 64 : 128;
+    for (int32_t r0 = 0; r0 < len; r0 += step) {
+      PfChunk c{};
+      c.x0 = start + r0;
+      c.nx = std::min(step, len - r0);
+      c.rows = step;
+      c.flags = rot ? PF_ROT : 0;
+      c.s = nullptr;  // resolved after the allocation (ones / zeros dummies)
+      c.e = nullptr;
+      c.b = nullptr;
+      if (E) {
+        if (E->flags & F_S) c.s = E->s;
+        if (E->flags & F_B) c.b = E->b;
+        if (E->flags & F_VERA) {
+          c.e = E->ve;
+          c.flags |= PF_VERA;
+        }
+        if (E->flags & F_TERM) {
+          c.Bp = (const uint16_t*)E->B;
+          c.rank = E->rank;
+          c.flags |= PF_OWN;
+        }
+      }
+      chunks.push_back(c);
+      // staged row sources: x rows by token, Delta rows as -(sorted position) - 1;
+      // rows past the chunk's tokens repeat its last one (computed, not stored)
+      for (int32_t r = 0; r < 128; ++r) {
+        if (rot && r >= 64)
+          crow.push_back(-(c.x0 + std::min(r - 64, c.nx - 1)) - 1);
+        else
+          crow.push_back(B->perm[c.x0 + std::min(r, c.nx - 1)]);
+      }
+    }
+  }
+  P.n_chunks = (int32_t)chunks.size();
+  if ((int64_t)P.n_chunks > 65535) return SCUTE_OK;  // grid y limit
+
+  // ---- prologue items ---------------------------------------------------------
+  std::vector<DecProItem> pro;
+  for (int32_t i = 0; i < B->nseg(); ++i) {
+    const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
+    const SlotEntry& E = L->table[a];
+    if (E.flags & F_R)
+      for (int32_t r0 = 0; r0 < len; r0 += 4)
+        for (int64_t c0 = 0; c0 < d_in; c0 += 64) {
+          DecProItem it{};
+          it.type = PRO_ROT;
+          it.p0 = start + r0;
+          it.n = std::min(4, len - r0);
+          it.k = (int32_t)c0;
+          for (int32_t r = 0; r < 4; ++r) it.tok[r] = B->perm[it.p0 + std::min(r, it.n - 1)];
+          it.ptr = (const uint16_t*)E.P;
+          it.blk = E.blk;
+          pro.push_back(it);
+        }
+    if (E.flags & F_TERM)
+      for (int32_t r0 = 0; r0 < len; r0 += 32)
+        for (int32_t k = 0; k < E.rank; k += 32)
+          for (int32_t kv = 0; kv < (int32_t)(d_in / 256); ++kv) {
+            DecProItem it{};
+            it.type = PRO_OSHRINK;
+            it.p0 = start + r0;
+            it.n = std::min(32, len - r0);
+            it.k = k | (std::min(32, E.rank - k) << 16);
+            it.ptr = (const uint16_t*)E.A;
+            it.blk = kv;
+            pro.push_back(it);
+          }
+  }
+  int32_t nvb = 0;
+  std::vector<DecVeraRow> vrows;
+  if (B->n_vera > 0) {
+    nvb = (B->n_vera + 31) / 32;
+    for (int32_t kv = 0; kv < (int32_t)(d_in / 256); ++kv)
+      for (int32_t vb = 0; vb < nvb; ++vb)
+        for (int32_t jb = 0; jb < L->r_v / 32; ++jb) {
+          DecProItem it{};
+          it.type = PRO_VSHRINK;
+          it.p0 = vb;
+          it.n = jb;
+          it.k = kv;
+          pro.push_back(it);
+        }
+    vrows.resize(32 * (size_t)nvb);
+    for (size_t v = 0; v < vrows.size(); ++v) {
+      const bool real = v < (size_t)B->n_vera;
+      const int32_t p = B->vera_pos[real ? v : 0];
+      vrows[v].vd = L->table[B->row_adapter[p]].vd;
+      vrows[v].tok = B->perm[p];
+      vrows[v].p = real ? p : -1;
+    }
+  }
+  // heaviest items first: they start on separate compute units
+  std::stable_sort(pro.begin(), pro.end(), [](const DecProItem& p, const DecProItem& q) {
+    auto rank = [](int32_t t) { return t == PRO_VSHRINK ? 0 : t == PRO_OSHRINK ? 1 : 2; };
+    return rank(p.type) < rank(q.type);
+  });
+  P.n_pro = (int32_t)pro.size();
+
+  // ---- one device allocation: tables, then the zeroed shrink buffers ----------
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o += al256(bytes);
+    return r;
+  };
+  const size_t o_chunks = take(sizeof(PfChunk) * chunks.size());
+  const size_t o_crow = take(4 * crow.size());
+  const size_t o_pro = take(sizeof(DecProItem) * pro.size() + 16);
+  const size_t o_vrows = take(sizeof(DecVeraRow) * vrows.size() + 16);
+  const size_t o_ones = take(4 * (size_t)d_out);
+  const size_t tables = o;
+  const size_t o_zeros = take(4 * (size_t)d_out);
+  const size_t acc_bytes = 4 * (size_t)n * P.AW;
+  if (acc_bytes >= ((size_t)1 << 31)) {
+    P = PrefillPlan{};  // buffer offsets are 32-bit
+    return SCUTE_OK;
+  }
+  const size_t o_acc0 = take(acc_bytes), o_acc1 = take(acc_bytes);
+  const size_t total = o;
+
+  hipError_t e = hipMalloc(&B->pf_dev, total);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(prefill plan)");
+  uint8_t* d = (uint8_t*)B->pf_dev;
+  const float* ones = (const float*)(d + o_ones);
+  const float* zeros = (const float*)(d + o_zeros);
+  for (PfChunk& c : chunks) {
+    if (!c.s) c.s = ones;
+    if (!c.e) c.e = ones;
+    if (!c.b) c.b = zeros;
+  }
+
+  std::vector<uint8_t> h(tables, 0);
+  memcpy(h.data() + o_chunks, chunks.data(), sizeof(PfChunk) * chunks.size());
+  memcpy(h.data() + o_crow, crow.data(), 4 * crow.size());
+  if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), sizeof(DecProItem) * pro.size());
+  if (!vrows.empty()) memcpy(h.data() + o_vrows, vrows.data(), sizeof(DecVeraRow) * vrows.size());
+  for (int64_t j = 0; j < d_out; ++j) {
+    const float one = 1.0f;
+    memcpy(h.data() + o_ones + 4 * j, &one, 4);
+  }
+  e = hipMemsetAsync(d + tables, 0, total - tables, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(d, h.data(), tables, hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    (void)hipFree(B->pf_dev);
+    B->pf_dev = nullptr;
+    P = PrefillPlan{};
+    return hip_fail(e, "upload prefill plan");
+  }
+  P.chunks = (const PfChunk*)(d + o_chunks);
+  P.crow = (const int32_t*)(d + o_crow);
+  P.pro_items = (const DecProItem*)(d + o_pro);
+  P.vrows = B->n_vera ? (const DecVeraRow*)(d + o_vrows) : nullptr;
+  P.acc32[0] = (float*)(d + o_acc0);
+  P.acc32[1] = (float*)(d + o_acc1);
+  P.acc_bytes = (uint32_t)acc_bytes;
+  P.fwd = 0;
+  P.enabled = true;
+  return SCUTE_OK;
+}
+
+}  // namespace scute

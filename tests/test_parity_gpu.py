@@ -133,10 +133,12 @@ def test_repeat_runs_and_plan_reuse():
     import os
     from lora_normal_form_amd import workload as glue
     os.environ["SCUTE_DECODE"] = "0"
+    os.environ["SCUTE_PREFILL"] = "0"
     try:
         ldg = glue.load(wl, device=0)
     finally:
         del os.environ["SCUTE_DECODE"]
+        del os.environ["SCUTE_PREFILL"]
     assert ldg.batch.info()["path"] == 0
     _, g1 = _run(wl, loaded=ldg)
     _, g2 = _run(wl, loaded=ldg)
