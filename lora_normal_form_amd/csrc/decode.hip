@@ -73,24 +73,6 @@ __device__ __forceinline__ void rotate_rows(const uint16_t* Pt, int32_t blk,
   }
 }
 
-// One 32x32 shrink tile over a K slice of 256 on 32x32x16 MFMA: lane (m, h)
-// holds row m of both operands (xr: its x row, ar: its A row, each already
-// offset to the slice and to the lane's 32-element half of every 64-element
-// block; the k order inside a block is permuted identically on both).
-// Element i of the result: operand-a row 8 (i / 4) + 4 h + i % 4, A row m.
-__device__ __forceinline__ f32x16 shrink_tile(const uint16_t* xr, const uint16_t* ar) {
-  uint4 xa[16], wa[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    xa[q] = ldg16(xr + 64 * (q >> 2) + 8 * (q & 3));
-    wa[q] = ldg16(ar + 64 * (q >> 2) + 8 * (q & 3));
-  }
-  f32x16 acc = {};
-#pragma unroll
-  for (int q = 0; q < 16; ++q) acc = mfma32(xa[q], wa[q], acc);
-  return acc;
-}
-
 // One wave per work-group, so consecutive items (the heavy VeRA-shrink items
 // come first) land on different compute units.
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2)))
@@ -214,21 +196,6 @@ k_decode_prologue(ProArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + a.RT + j, acc[i] * dsc[i]);
-    } else if (item.type == PRO_OSHRINK) {
-      // own-term shrink on MFMA (long segments): 32 sorted rows of one adapter
-      // x 32 ranks of its A' over one K slice of 256; lanes past the rows or
-      // ranks repeat the last one and their sums are not stored
-      const int32_t p0 = item.p0, nr = item.n, k0 = item.k & 0xFFFF, nk = item.k >> 16;
-      const int m = lane & 31, h = lane >> 5;
-      const int64_t koff = (int64_t)item.blk * 256 + 32 * h;
-      const int32_t tok = ldg(a.perm + p0 + min(m, nr - 1));
-      const f32x16 acc = shrink_tile(a.x + (size_t)tok * d_in + koff,
-                                     item.ptr + (size_t)(k0 + min(m, nk - 1)) * d_in + koff);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * h + (i & 3);
-        if (row < nr && m < nk) atomicAdd(a.acc + (size_t)(p0 + row) * a.AW + k0 + m, acc[i]);
-      }
     }
   }
 }
@@ -764,7 +731,6 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   {
     ProArgs pa{};
     pa.x = (const uint16_t*)x;
-    pa.perm = B->d_perm;
     pa.items = D.pro_items;
     pa.n_items = D.n_pro;
     pa.vrows = D.vrows;

@@ -100,10 +100,7 @@ struct DecRow {
 //                ptr = A', blk = K part (1024 wide)
 //   VeRA shrink: p0 = block of 32 VeRA rows, n = block of 32 ranks,
 //                k = K slice (256 wide)
-//   own shrink on MFMA (prefill): p0 = first of up to 32 sorted rows of one
-//                adapter, n = rows, k = first rank | ranks (<= 32) << 16,
-//                ptr = A', blk = K slice (256 wide)
-enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3, PRO_OSHRINK = 4 };
+enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3 };
 // expand item kinds of the decode main kernel
 enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
 struct DecProItem {
@@ -170,20 +167,44 @@ struct PfChunk {
 };
 enum : int32_t { PF_OWN = 1, PF_VERA = 2, PF_ROT = 4 };
 
+// Prologue item of the prefill path (one work-group of 16 waves each):
+//   shrink:      rows p0 .. p0 + n - 1 (sorted positions, n <= 32) x own
+//                ranks (k & 0xFFFF) .. + (k >> 16) (<= 32) of A' = ptr, full K
+//   VeRA shrink: VeRA rows 32 p0 .. + 31 (of the VeRA row table) x ranks
+//                32 k .. 32 k + 31 of A_sh, full K, scaled by d
+//   rotation:    Delta rows p0 .. p0 + n - 1 (n <= 32) x columns k .. k + 1023,
+//                ptr = (R - I)^T blocks of size blk
+// 32 bytes.
+enum : int32_t { PP_SHRINK = 0, PP_VSHRINK = 1, PP_ROT = 2 };
+struct PfProItem {
+  int32_t type, p0, n, k;
+  const uint16_t* ptr;
+  int32_t blk, pad;
+};
+
 struct PrefillPlan {
   bool enabled = false;
   int32_t n_chunks = 0;
   int32_t C = 0;        // column tiles of 256 outputs
+  // work-groups of the main kernel: {column tile, chunk, K part (-1: the
+  // whole K), exchange slot}; whole tiles first, then P parts of each tile
+  // of the remainder
+  const int4* items = nullptr;
+  int32_t n_items = 0;
+  int32_t P = 1;        // K parts of a split tile (1, 2 or 4)
+  int32_t n_split = 0;  // split tiles
+  float* part = nullptr;      // [n_split][P][32][256] f32x4 partial tiles
+  int32_t* cnt = nullptr;     // [n_split] arrival counters (kept at zero)
+  uint32_t part_bytes = 0;
   int32_t RT = 0;       // own-term ranks per row in the shrink buffer (max rank, to 16)
   int32_t AW = 0;       // shrink buffer row: RT own ranks, then r_v VeRA ranks
   int32_t n_pro = 0;    // prologue work items
   const PfChunk* chunks = nullptr;        // [n_chunks]
   const int32_t* crow = nullptr;          // [n_chunks][128] staged row sources
-  const DecProItem* pro_items = nullptr;  // rotation, shrinks
-  const DecVeraRow* vrows = nullptr;      // [32 nvb]
-  float* acc32[2] = {nullptr, nullptr};   // per parity: [n][AW] fp32 shrink sums
+  const PfProItem* pro_items = nullptr;  // shrinks, rotation
+  const DecVeraRow* vrows = nullptr;     // [32 nvb]
+  float* acc32 = nullptr;                // [n][AW] fp32 shrink sums (each written once per forward)
   uint32_t acc_bytes = 0;
-  mutable uint32_t fwd = 0;
 };
 
 }  // namespace scute
@@ -247,11 +268,9 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
 scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                             float* y, hipStream_t st, int32_t* launches);
 
-// Arguments of the prologue kernel (decode.hip), shared by the decode and
-// prefill paths.
+// Arguments of the decode path's prologue kernel (decode.hip).
 struct ProArgs {
   const uint16_t* x;
-  const int32_t* perm;      // sorted position -> token (own-term MFMA shrink items)
   const DecProItem* items;
   int32_t n_items;
   const DecVeraRow* vrows;  // [32 nvb]

@@ -121,4 +121,22 @@ __device__ __forceinline__ uint32_t pack_bf2(uint32_t lo, uint32_t hi) {
   return (uint32_t)f2bf(__uint_as_float(lo)) | ((uint32_t)f2bf(__uint_as_float(hi)) << 16);
 }
 
+// One 32x32 shrink tile over a K slice of 256 on 32x32x16 MFMA: lane (m, h)
+// holds row m of both operands (xr: its x row, ar: its A row, each already
+// offset to the slice and to the lane's 32-element half of every 64-element
+// block; the k order inside a block is permuted identically on both).
+// Element i of the result: operand-a row 8 (i / 4) + 4 h + i % 4, A row m.
+__device__ __forceinline__ f32x16 shrink_tile(const uint16_t* xr, const uint16_t* ar,
+                                               f32x16 acc = f32x16{}) {
+  uint4 xa[16], wa[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    xa[q] = ldg16(xr + 64 * (q >> 2) + 8 * (q & 3));
+    wa[q] = ldg16(ar + 64 * (q >> 2) + 8 * (q & 3));
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc = mfma32(xa[q], wa[q], acc);
+  return acc;
+}
+
 }  // namespace scute

@@ -9,8 +9,9 @@
 // chunk is up to 128 tokens of a segment, or up to 64 tokens and their 64
 // Delta rows when the adapter rotates. The expand runs in the same epilogue
 // as extra MFMA steps whose A operand is the chunk's shrink sums.
-// The prologue (rotation Delta = x (R - I), own-term and VeRA shrinks) uses
-// the decode path's prologue kernel with MFMA shrink items.
+// The prologue kernel computes the own-term and VeRA shrinks (tiles of 32
+// rows x 32 ranks over the whole K, so every sum is written once, in a fixed
+// order) and the rotation Delta = x (R - I).
 
 #include <string.h>
 
@@ -40,7 +41,9 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   if (L->act != SCUTE_BF16 || n <= 0) return SCUTE_OK;
   // the main kernel's K loop is unrolled for 64 stages of 64
   if (d_in != 4096 || d_out % 256 != 0) return SCUTE_OK;
-  if (d_in * d_out * 2 >= ((int64_t)1 << 32)) return SCUTE_OK;
+  // W, x and the Delta rows are addressed through buffer ranges with 32-bit offsets
+  if (d_in * d_out * 2 >= ((int64_t)1 << 32) || (int64_t)n * d_in * 2 >= ((int64_t)1 << 32))
+    return SCUTE_OK;
   if (B->n_rot > 0 && !B->delta) return SCUTE_OK;
   if (B->n_vera > 0 && L->r_v % 64 != 0) return SCUTE_OK;
   for (int32_t i = 0; i < B->nseg(); ++i) {
@@ -104,54 +107,87 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
     }
   }
   P.n_chunks = (int32_t)chunks.size();
-  if ((int64_t)P.n_chunks > 65535) return SCUTE_OK;  // grid y limit
+
+  // ---- work-group order --------------------------------------------------------
+  // Work-groups are dispatched round-robin over the 8 XCDs by linear id, and
+  // each XCD has its own L2. Each XCD gets a block of cg column tiles x a
+  // share of the chunks (cg chosen so the W and rows one XCD reads are
+  // smallest), chunk-major, so the work-groups running together on an XCD
+  // share W columns and rows. Every XCD runs whole tiles in multiples of its
+  // compute units; the tiles left over are split into P parts of the K
+  // dimension (as many as the idle compute units take, up to 4) whose
+  // partial tiles meet in a workspace.
+  const int32_t X = 8;
+  const int32_t cu = L->num_cu > 0 ? L->num_cu : 256;
+  const int32_t cpx = std::max(1, cu / X);
+  int32_t cg = 1;
+  {
+    double best = 1e300;
+    for (int32_t g = 1; g <= X && g <= P.C; g *= 2) {
+      const int32_t rg = X / g;
+      const double bytes = (double)((P.C + g - 1) / g) * 256.0 + (double)((P.n_chunks + rg - 1) / rg) * 128.0;
+      if (bytes < best) {
+        best = bytes;
+        cg = g;
+      }
+    }
+  }
+  const int32_t rg = X / cg;
+  std::vector<std::vector<int4>> full(X);
+  std::vector<int4> rest;
+  for (int32_t x = 0; x < X; ++x) {
+    const int32_t c_lo = P.C * (x % cg) / cg, c_hi = P.C * (x % cg + 1) / cg;
+    const int32_t r_lo = P.n_chunks * (x / cg) / rg, r_hi = P.n_chunks * (x / cg + 1) / rg;
+    std::vector<int4> lst;
+    for (int32_t ci = r_lo; ci < r_hi; ++ci)
+      for (int32_t c = c_lo; c < c_hi; ++c) lst.push_back(make_int4(c, ci, -1, 0));
+    const size_t nf = lst.size() / cpx * cpx;
+    full[x].assign(lst.begin(), lst.begin() + nf);
+    rest.insert(rest.end(), lst.begin() + nf, lst.end());
+  }
+  int32_t parts = 1;
+  while (parts < 4 && !rest.empty() && (int64_t)rest.size() * parts * 2 <= cu) parts *= 2;
+  parts = env_int("SCUTE_PREFILL_PARTS", parts);
+  if (parts != 1 && parts != 2 && parts != 4)
+    return fail(SCUTE_E_INVALID, "bad SCUTE_PREFILL_PARTS (1, 2 or 4)");
+  std::vector<int4> items;
+  for (size_t j = 0;; ++j) {
+    bool any = false;
+    for (int32_t x = 0; x < X; ++x)
+      if (j < full[x].size()) {
+        items.push_back(full[x][j]);
+        any = true;
+      }
+    if (!any) break;
+  }
+  for (size_t t = 0; t < rest.size(); ++t)
+    for (int32_t q = 0; q < parts; ++q)
+      items.push_back(make_int4(rest[t].x, rest[t].y, parts > 1 ? q : -1, (int32_t)t));
+  P.n_items = (int32_t)items.size();
+  P.P = parts;
+  P.n_split = parts > 1 ? (int32_t)rest.size() : 0;
 
   // ---- prologue items ---------------------------------------------------------
-  std::vector<DecProItem> pro;
+  // shrink tiles of 32 rows x 32 ranks over the full K (own: per segment;
+  // VeRA: over the table of VeRA rows), then rotation tiles of 32 rows x 1024
+  // columns
+  std::vector<PfProItem> pro;
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
-    if (E.flags & F_R)
-      for (int32_t r0 = 0; r0 < len; r0 += 4)
-        for (int64_t c0 = 0; c0 < d_in; c0 += 64) {
-          DecProItem it{};
-          it.type = PRO_ROT;
-          it.p0 = start + r0;
-          it.n = std::min(4, len - r0);
-          it.k = (int32_t)c0;
-          for (int32_t r = 0; r < 4; ++r) it.tok[r] = B->perm[it.p0 + std::min(r, it.n - 1)];
-          it.ptr = (const uint16_t*)E.P;
-          it.blk = E.blk;
-          pro.push_back(it);
-        }
     if (E.flags & F_TERM)
       for (int32_t r0 = 0; r0 < len; r0 += 32)
         for (int32_t k = 0; k < E.rank; k += 32)
-          for (int32_t kv = 0; kv < (int32_t)(d_in / 256); ++kv) {
-            DecProItem it{};
-            it.type = PRO_OSHRINK;
-            it.p0 = start + r0;
-            it.n = std::min(32, len - r0);
-            it.k = k | (std::min(32, E.rank - k) << 16);
-            it.ptr = (const uint16_t*)E.A;
-            it.blk = kv;
-            pro.push_back(it);
-          }
+          pro.push_back(PfProItem{PP_SHRINK, start + r0, std::min(32, len - r0),
+                                  k | (std::min(32, E.rank - k) << 16), (const uint16_t*)E.A, 0, 0});
   }
   int32_t nvb = 0;
   std::vector<DecVeraRow> vrows;
   if (B->n_vera > 0) {
     nvb = (B->n_vera + 31) / 32;
-    for (int32_t kv = 0; kv < (int32_t)(d_in / 256); ++kv)
-      for (int32_t vb = 0; vb < nvb; ++vb)
-        for (int32_t jb = 0; jb < L->r_v / 32; ++jb) {
-          DecProItem it{};
-          it.type = PRO_VSHRINK;
-          it.p0 = vb;
-          it.n = jb;
-          it.k = kv;
-          pro.push_back(it);
-        }
+    for (int32_t vb = 0; vb < nvb; ++vb)
+      for (int32_t jb = 0; jb < L->r_v / 32; ++jb)
+        pro.push_back(PfProItem{PP_VSHRINK, vb, 32, jb, nullptr, 0, 0});
     vrows.resize(32 * (size_t)nvb);
     for (size_t v = 0; v < vrows.size(); ++v) {
       const bool real = v < (size_t)B->n_vera;
@@ -161,14 +197,18 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
       vrows[v].p = real ? p : -1;
     }
   }
-  // heaviest items first: they start on separate compute units
-  std::stable_sort(pro.begin(), pro.end(), [](const DecProItem& p, const DecProItem& q) {
-    auto rank = [](int32_t t) { return t == PRO_VSHRINK ? 0 : t == PRO_OSHRINK ? 1 : 2; };
-    return rank(p.type) < rank(q.type);
-  });
+  for (int32_t i = 0; i < B->nseg(); ++i) {
+    const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
+    const SlotEntry& E = L->table[a];
+    if (E.flags & F_R)
+      for (int32_t r0 = 0; r0 < len; r0 += 32)
+        for (int64_t c0 = 0; c0 < d_in; c0 += 1024)
+          pro.push_back(PfProItem{PP_ROT, start + r0, std::min(32, len - r0), (int32_t)c0,
+                                  (const uint16_t*)E.P, E.blk, 0});
+  }
   P.n_pro = (int32_t)pro.size();
 
-  // ---- one device allocation: tables, then the zeroed shrink buffers ----------
+  // ---- one device allocation: tables, then the shrink sums ----------------------
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t r = o;
@@ -176,8 +216,9 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
     return r;
   };
   const size_t o_chunks = take(sizeof(PfChunk) * chunks.size());
+  const size_t o_items = take(sizeof(int4) * items.size());
   const size_t o_crow = take(4 * crow.size());
-  const size_t o_pro = take(sizeof(DecProItem) * pro.size() + 16);
+  const size_t o_pro = take(sizeof(PfProItem) * pro.size() + 16);
   const size_t o_vrows = take(sizeof(DecVeraRow) * vrows.size() + 16);
   const size_t o_ones = take(4 * (size_t)d_out);
   const size_t tables = o;
@@ -187,7 +228,13 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
     P = PrefillPlan{};  // buffer offsets are 32-bit
     return SCUTE_OK;
   }
-  const size_t o_acc0 = take(acc_bytes), o_acc1 = take(acc_bytes);
+  const size_t o_acc = take(acc_bytes);
+  const size_t part_bytes = (size_t)P.n_split * parts * 32 * 256 * 16;
+  if (part_bytes >= ((size_t)1 << 31)) {
+    P = PrefillPlan{};
+    return SCUTE_OK;
+  }
+  const size_t o_part = take(part_bytes), o_cnt = take(4 * (size_t)P.n_split + 4);
   const size_t total = o;
 
   hipError_t e = hipMalloc(&B->pf_dev, total);
@@ -203,8 +250,9 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
 
   std::vector<uint8_t> h(tables, 0);
   memcpy(h.data() + o_chunks, chunks.data(), sizeof(PfChunk) * chunks.size());
+  memcpy(h.data() + o_items, items.data(), sizeof(int4) * items.size());
   memcpy(h.data() + o_crow, crow.data(), 4 * crow.size());
-  if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), sizeof(DecProItem) * pro.size());
+  if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), sizeof(PfProItem) * pro.size());
   if (!vrows.empty()) memcpy(h.data() + o_vrows, vrows.data(), sizeof(DecVeraRow) * vrows.size());
   for (int64_t j = 0; j < d_out; ++j) {
     const float one = 1.0f;
@@ -221,12 +269,14 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   }
   P.chunks = (const PfChunk*)(d + o_chunks);
   P.crow = (const int32_t*)(d + o_crow);
-  P.pro_items = (const DecProItem*)(d + o_pro);
+  P.pro_items = (const PfProItem*)(d + o_pro);
   P.vrows = B->n_vera ? (const DecVeraRow*)(d + o_vrows) : nullptr;
-  P.acc32[0] = (float*)(d + o_acc0);
-  P.acc32[1] = (float*)(d + o_acc1);
+  P.items = (const int4*)(d + o_items);
+  P.part = (float*)(d + o_part);
+  P.cnt = (int32_t*)(d + o_cnt);
+  P.part_bytes = (uint32_t)part_bytes;
+  P.acc32 = (float*)(d + o_acc);
   P.acc_bytes = (uint32_t)acc_bytes;
-  P.fwd = 0;
   P.enabled = true;
   return SCUTE_OK;
 }
