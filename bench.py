@@ -95,6 +95,19 @@ def time_forwards(torch, sets, steps, warmup, profile=False):
     return gpu_ms, wall, kernels
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def dominant_kernel_flops(name, cost):
+    """Algorithmic flops of one launch of an MFMA-bound kernel (None for the
+    HBM-bound ones): prefill_main computes the base GEMM (x W) and the
+    expands (t B', u B_sh); its second pass over W for the rotated rows'
+    Delta is not counted, since the method itself computes (x R) W once."""
+    if name == "prefill_main":
+        return cost["gemm_flops"]
+    return None
+
+
 def dominant_kernel_bytes(name, wl, cost):
     """Algorithmic bytes one launch of kernel ``name`` must move.
 
@@ -205,7 +218,16 @@ def main():
         k = kern[dom]
         avg_s = k["total_ms"] / max(1, k["launches"]) * 1e-3
         kb = dominant_kernel_bytes(dom, wl, cost)
-        if kb is not None:
+        kf = dominant_kernel_flops(dom, cost)
+        if kf is not None:
+            ach = kf / avg_s / 1e12
+            tr = measured_traffic(dom, wl)
+            roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": None if tr is None else round(tr),
+                    "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 3),
+                    "flops_per_launch": kf}
+        elif kb is not None:
             ach = kb / avg_s / 1e9
             tr = measured_traffic(dom, wl)
             roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,

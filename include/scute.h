@@ -115,6 +115,9 @@ typedef struct scute_cost {
   /* the same bytes split by the step that needs them (x counted in both):  */
   double gemm_bytes;     /* base GEMM + expand: x, W, y, B', s, b, VeRA e, B_sh */
   double prologue_bytes; /* rotation + shrink: x, A', P, VeRA d, A_sh          */
+  /* the flops split the same way:                                           */
+  double gemm_flops;     /* 2 n d_in d_out + expands (t B', u B_sh)           */
+  double prologue_flops; /* shrinks (x A', x A_sh) + rotations (x P)          */
 } scute_cost;
 
 /* Create a layer context for one (d_in, d_out, activation dtype, device).

@@ -204,7 +204,7 @@ extern "C" scute_status scute_cost_model(const scute_layer* L, const scute_batch
   memset(out, 0, sizeof(*out));
   const double es = (double)dtype_size(L->act);
   const double n = B->n, din = (double)L->d_in, dout = (double)L->d_out;
-  double adapter = 0.0, flops_extra = 0.0, gemm_side = 0.0, pro_side = 0.0;
+  double adapter = 0.0, flops_extra = 0.0, gemm_side = 0.0, pro_side = 0.0, exp_flops = 0.0;
   bool any_pro = false;
   bool any_vera = false;
   std::vector<char> seen(L->max_adapters, 0);
@@ -221,10 +221,14 @@ extern "C" scute_status scute_cost_model(const scute_layer* L, const scute_batch
       pro_side += (double)(S.len[SCUTE_SLOT_A] + S.len[SCUTE_SLOT_VD] + S.len[SCUTE_SLOT_P]);
     }
     if (E.flags & (F_TERM | F_VERA | F_R)) any_pro = true;
-    if (E.flags & F_TERM) flops_extra += 2.0 * (din * E.rank + E.rank * dout);
+    if (E.flags & F_TERM) {
+      flops_extra += 2.0 * (din * E.rank + E.rank * dout);
+      exp_flops += 2.0 * E.rank * dout;
+    }
     if (E.flags & F_VERA) {
       any_vera = true;
       flops_extra += 2.0 * (din * L->r_v + L->r_v * dout);
+      exp_flops += 2.0 * L->r_v * dout;
     }
     if (E.flags & F_R) flops_extra += 2.0 * din * E.blk;
   }
@@ -239,6 +243,8 @@ extern "C" scute_status scute_cost_model(const scute_layer* L, const scute_batch
   out->adapter_bytes = adapter;
   out->base_flops = 2.0 * n * din * dout;
   out->flops = out->base_flops + flops_extra;
+  out->gemm_flops = out->base_flops + exp_flops;
+  out->prologue_flops = flops_extra - exp_flops;
   out->launches = forward_launch_count(L, B);
   out->n_tokens = B->n;
   out->n_segments = B->nseg();

@@ -41,11 +41,16 @@ def source_sha() -> str:
     return h.hexdigest()
 
 
+def _plain(name: str) -> str:
+    """Kernel name without its parameter list and anonymous namespaces."""
+    return name.replace("(anonymous namespace)::", "").split("(")[0]
+
+
 def short_name(name: str):
     """The library's name for one of its kernels (the name bench.py and
     scute_profile_read use: "decode_main", "gemm", ...), or None for kernels
     that are not the library's."""
-    base = name.split("(")[0]
+    base = _plain(name)
     if "scute::" not in base:
         return None
     base = base[base.index("scute::") + len("scute::"):].split("<")[0]
@@ -57,7 +62,7 @@ def stats_table(path: str) -> str:
     total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
     out = ["| kernel | calls | average (us) | share |", "|---|---|---|---|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        out.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | "
+        out.append(f"| `{_plain(r['Name'])}` | {r['Calls']} | "
                    f"{float(r['AverageNs']) / 1e3:.2f} | "
                    f"{100.0 * float(r['TotalDurationNs']) / total:.1f}% |")
     return "\n".join(out)

@@ -50,7 +50,8 @@ class Cost(C.Structure):
                 ("base_flops", C.c_double), ("launches", C.c_int32), ("n_tokens", C.c_int32),
                 ("n_segments", C.c_int32), ("n_rot_rows", C.c_int32),
                 ("n_vera_rows", C.c_int32), ("n_touched", C.c_int32),
-                ("gemm_bytes", C.c_double), ("prologue_bytes", C.c_double)]
+                ("gemm_bytes", C.c_double), ("prologue_bytes", C.c_double),
+                ("gemm_flops", C.c_double), ("prologue_flops", C.c_double)]
 
 
 class AdapterInfo(C.Structure):
