@@ -167,12 +167,14 @@ struct PfChunk {
 };
 enum : int32_t { PF_OWN = 1, PF_VERA = 2, PF_ROT = 4 };
 
-// Prologue item of the prefill path (one work-group of 16 waves each):
-//   shrink:      rows p0 .. p0 + n - 1 (sorted positions, n <= 32) x own
-//                ranks (k & 0xFFFF) .. + (k >> 16) (<= 32) of A' = ptr, full K
-//   VeRA shrink: VeRA rows 32 p0 .. + 31 (of the VeRA row table) x ranks
-//                32 k .. 32 k + 31 of A_sh, full K, scaled by d
-//   rotation:    Delta rows p0 .. p0 + n - 1 (n <= 32) x columns k .. k + 1023,
+// Prologue item of the prefill path (one work-group of 4 waves each):
+//   shrink:      rows p0 .. p0 + n - 1 (sorted positions, n <= 64) x own
+//                ranks (k & 0xFFFF) .. + (k >> 16) (<= 64) of A' = ptr, over
+//                K part blk (1024 wide)
+//   VeRA shrink: VeRA rows 64 p0 .. + 63 (of the VeRA row table) x ranks
+//                (k & 0xFFFF) .. + 63 of A_sh over K part blk, scaled by d
+//   (shrinks: pad = the tile's arrival counter)
+//   rotation:    Delta rows p0 .. p0 + n - 1 (n <= 32) x columns k .. k + 255,
 //                ptr = (R - I)^T blocks of size blk
 // 32 bytes.
 enum : int32_t { PP_SHRINK = 0, PP_VSHRINK = 1, PP_ROT = 2 };
@@ -202,9 +204,15 @@ struct PrefillPlan {
   const PfChunk* chunks = nullptr;        // [n_chunks]
   const int32_t* crow = nullptr;          // [n_chunks][128] staged row sources
   const PfProItem* pro_items = nullptr;  // shrinks, rotation
-  const DecVeraRow* vrows = nullptr;     // [32 nvb]
-  float* acc32 = nullptr;                // [n][AW] fp32 shrink sums (each written once per forward)
+  const DecVeraRow* vrows = nullptr;     // [64 nvb]
+  // per parity: [n][AW] shrink sums in fixed point (int64, units of 2^-32);
+  // forwards alternate between the two and each prologue clears the other
+  long long* acc64[2] = {nullptr, nullptr};
   uint32_t acc_bytes = 0;
+  mutable uint32_t fwd = 0;
+  uint16_t* tbf = nullptr;    // [n][AW] the finished sums in bf16 (the expand's A operand)
+  int32_t* tcnt = nullptr;    // [shrink tiles] arrival counters of the K parts (kept at zero)
+  uint32_t tbf_bytes = 0;
 };
 
 }  // namespace scute

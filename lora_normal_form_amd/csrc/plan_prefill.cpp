@@ -9,9 +9,9 @@
 // chunk is up to 128 tokens of a segment, or up to 64 tokens and their 64
 // Delta rows when the adapter rotates. The expand runs in the same epilogue
 // as extra MFMA steps whose A operand is the chunk's shrink sums.
-// The prologue kernel computes the own-term and VeRA shrinks (tiles of 32
-// rows x 32 ranks over the whole K, so every sum is written once, in a fixed
-// order) and the rotation Delta = x (R - I).
+// The prologue kernel computes the own-term and VeRA shrinks (tiles of 64
+// rows x 64 ranks x one K part of 1024, added in fixed point so the sums do
+// not depend on the order of the parts) and the rotation Delta = x (R - I).
 
 #include <string.h>
 
@@ -168,27 +168,32 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   P.n_split = parts > 1 ? (int32_t)rest.size() : 0;
 
   // ---- prologue items ---------------------------------------------------------
-  // shrink tiles of 32 rows x 32 ranks over the full K (own: per segment;
-  // VeRA: over the table of VeRA rows), then rotation tiles of 32 rows x 1024
-  // columns
+  // shrink tiles of 64 rows x 64 ranks over one K part of 1024 (own: per
+  // segment; VeRA: over the table of VeRA rows), then rotation tiles of 32
+  // rows x 256 columns
+  const int32_t KP = (int32_t)(d_in / 1024);
   std::vector<PfProItem> pro;
+  int32_t n_tiles = 0;  // shrink tiles (each with an arrival counter)
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
     if (E.flags & F_TERM)
-      for (int32_t r0 = 0; r0 < len; r0 += 32)
-        for (int32_t k = 0; k < E.rank; k += 32)
-          pro.push_back(PfProItem{PP_SHRINK, start + r0, std::min(32, len - r0),
-                                  k | (std::min(32, E.rank - k) << 16), (const uint16_t*)E.A, 0, 0});
+      for (int32_t r0 = 0; r0 < len; r0 += 64)
+        for (int32_t k = 0; k < E.rank; k += 64, ++n_tiles)
+          for (int32_t kp = 0; kp < KP; ++kp)
+            pro.push_back(PfProItem{PP_SHRINK, start + r0, std::min(64, len - r0),
+                                    k | (std::min(64, E.rank - k) << 16), (const uint16_t*)E.A, kp,
+                                    n_tiles});
   }
   int32_t nvb = 0;
   std::vector<DecVeraRow> vrows;
   if (B->n_vera > 0) {
-    nvb = (B->n_vera + 31) / 32;
+    nvb = (B->n_vera + 63) / 64;
     for (int32_t vb = 0; vb < nvb; ++vb)
-      for (int32_t jb = 0; jb < L->r_v / 32; ++jb)
-        pro.push_back(PfProItem{PP_VSHRINK, vb, 32, jb, nullptr, 0, 0});
-    vrows.resize(32 * (size_t)nvb);
+      for (int32_t k = 0; k < L->r_v; k += 64, ++n_tiles)
+        for (int32_t kp = 0; kp < KP; ++kp)
+          pro.push_back(PfProItem{PP_VSHRINK, vb, 64, k | (64 << 16), nullptr, kp, n_tiles});
+    vrows.resize(64 * (size_t)nvb);
     for (size_t v = 0; v < vrows.size(); ++v) {
       const bool real = v < (size_t)B->n_vera;
       const int32_t p = B->vera_pos[real ? v : 0];
@@ -202,7 +207,7 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
     const SlotEntry& E = L->table[a];
     if (E.flags & F_R)
       for (int32_t r0 = 0; r0 < len; r0 += 32)
-        for (int64_t c0 = 0; c0 < d_in; c0 += 1024)
+        for (int64_t c0 = 0; c0 < d_in; c0 += 256)
           pro.push_back(PfProItem{PP_ROT, start + r0, std::min(32, len - r0), (int32_t)c0,
                                   (const uint16_t*)E.P, E.blk, 0});
   }
@@ -223,12 +228,14 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   const size_t o_ones = take(4 * (size_t)d_out);
   const size_t tables = o;
   const size_t o_zeros = take(4 * (size_t)d_out);
-  const size_t acc_bytes = 4 * (size_t)n * P.AW;
+  const size_t acc_bytes = 8 * (size_t)n * P.AW;
   if (acc_bytes >= ((size_t)1 << 31)) {
     P = PrefillPlan{};  // buffer offsets are 32-bit
     return SCUTE_OK;
   }
-  const size_t o_acc = take(acc_bytes);
+  const size_t o_acc0 = take(acc_bytes), o_acc1 = take(acc_bytes);
+  const size_t tbf_bytes = 2 * (size_t)n * P.AW;
+  const size_t o_tbf = take(tbf_bytes), o_tcnt = take(4 * (size_t)n_tiles + 4);
   const size_t part_bytes = (size_t)P.n_split * parts * 32 * 256 * 16;
   if (part_bytes >= ((size_t)1 << 31)) {
     P = PrefillPlan{};
@@ -275,8 +282,13 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   P.part = (float*)(d + o_part);
   P.cnt = (int32_t*)(d + o_cnt);
   P.part_bytes = (uint32_t)part_bytes;
-  P.acc32 = (float*)(d + o_acc);
+  P.acc64[0] = (long long*)(d + o_acc0);
+  P.acc64[1] = (long long*)(d + o_acc1);
   P.acc_bytes = (uint32_t)acc_bytes;
+  P.fwd = 0;
+  P.tbf = (uint16_t*)(d + o_tbf);
+  P.tcnt = (int32_t*)(d + o_tcnt);
+  P.tbf_bytes = (uint32_t)tbf_bytes;
   P.enabled = true;
   return SCUTE_OK;
 }

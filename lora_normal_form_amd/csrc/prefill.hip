@@ -3,14 +3,17 @@
 //
 // Two kernels per forward.
 //
-// k_prefill_prologue works on items of one work-group (16 waves) each:
-//   shrink       t = x A' for 32 rows of a segment x 32 own ranks, and
-//   VeRA shrink  u = (x A_sh) (.) d for 32 VeRA rows x 32 ranks, both over the
-//                whole K on 32x32x16 bf16 MFMA (16 waves, wave w sums K slice
-//                w; the slices meet in LDS in a fixed order, so the sums are
-//                the same on every forward and are stored once, without
-//                atomics);
-//   rotation     Delta = x (R - I) for 32 rotated rows x 1024 columns; R is
+// k_prefill_prologue works on items of one work-group (4 waves) each:
+//   shrink       t = x A' for 64 rows of a segment x 64 own ranks, and
+//   VeRA shrink  u = (x A_sh) (.) d for 64 VeRA rows x 64 ranks, both over
+//                one K part of 1024 on 32x32x16 bf16 MFMA, operands staged in
+//                LDS by direct loads; the parts add into fixed-point sums
+//                with integer atomics (order-independent, so every forward
+//                gives the same bits), and the last part of a tile to arrive
+//                converts the tile's sums to bf16 for the main kernel; the
+//                fixed-point sums alternate between two buffers and each
+//                prologue clears the one the next forward uses;
+//   rotation     Delta = x (R - I) for 32 rotated rows x 256 columns; R is
 //                block diagonal, so each 32-column MFMA block contracts over
 //                one diagonal block.
 //
@@ -29,8 +32,8 @@
 //            wait is exact.
 //   epilogue Delta W folds into the token rows (rows 64 + r onto r, in
 //            registers), the base product is scaled by s, the expand runs as
-//            extra MFMA steps: A = the chunk's shrink sums (fp32 rounded to
-//            bf16, staged through the ring in pieces of 64 ranks), B = the
+//            extra MFMA steps: A = the chunk's shrink sums (bf16, staged
+//            through the ring in pieces of 64 ranks), B = the
 //            adapter's B' rows, or the shared B_sh rows scaled by e (VeRA:
 //            ((x A_sh) (.) d) B_sh (.) e, with e folded into B per column),
 //            then b is added and the token rows are stored.
@@ -48,6 +51,18 @@ namespace scute {
 
 namespace {
 
+// Shrink sums are kept in fixed point: int64 in units of 2^-32. Every K
+// slice of a shrink adds its partial sums with integer atomics, which are
+// associative, so the totals do not depend on the order the slices land in
+// (the same bits on every forward). A partial below 2^-9 in magnitude keeps
+// fewer than its 24 bits (absolute error <= 2^-33); values stay far below
+// the 2^31 range.
+constexpr float FX_SCALE = 4294967296.0f;  // 2^32
+__device__ __forceinline__ unsigned long long fx_from(float v) {
+  return (unsigned long long)__float2ll_rn(v * FX_SCALE);
+}
+__device__ __forceinline__ float fx_to(long long v) { return (float)((double)v * 0x1p-32); }
+
 struct PfArgs {
   const uint16_t* x;       // [n][d_in] rows in batch (token) order
   const uint16_t* dx;      // [n_rot][d_in] Delta rows by sorted position
@@ -55,7 +70,7 @@ struct PfArgs {
   const PfChunk* chunks;   // [n_chunks]
   const int32_t* crow;     // [n_chunks][128] row sources: token, or -(Delta row) - 1
   const uint16_t* B_sh;    // [d_out][r_v]
-  const float* acc;        // [n][AW] shrink sums: RT own ranks, then r_v VeRA ranks
+  const uint16_t* tbf;     // [n][AW] shrink sums in bf16: RT own ranks, then r_v VeRA ranks
   float* y;                // [n][d_out]
   const int4* items;        // per work-group: column tile, chunk, K part (-1: all), exchange slot
   float* part;              // [n_split][P][32][256] f32x4 partial tiles
@@ -333,7 +348,7 @@ k_prefill_main(PfArgs a) {
   const int n_own = (flags & PF_OWN) ? (rank + 63) / 64 : 0;
   const int n_ver = (flags & PF_VERA) ? a.r_v / 64 : 0;
   const int ntok = rot ? 64 : 128;  // token rows of the tile
-  const rsrc_t ar = make_rsrc(a.acc, a.acc_bytes);
+  const rsrc_t ar = make_rsrc(a.tbf, a.acc_bytes);
   for (int pc = 0; pc < n_own + n_ver; ++pc) {
     const bool own = pc < n_own;
     const int kp0 = own ? 64 * pc : 64 * (pc - n_own);
@@ -351,27 +366,18 @@ k_prefill_main(PfArgs a) {
         bf[cb][s] = k < len ? ldg16(bbase + (size_t)(col0 + 32 * cb) * len + k) : make_uint4(0, 0, 0, 0);
       }
     // A operand: thread -> row tid / 2, ranks 32 (tid % 2) .. + 31 of the
-    // piece, fp32 sums rounded to bf16 into the staged layout
+    // piece (bf16 sums) into the staged layout
     {
       const int r = tid >> 1, hh = tid & 1;
       const bool rowok = r < ntok && r < ch.nx;
-      const uint32_t base = (uint32_t)((((int64_t)ch.x0 + r) * a.AW + acol + kp0 + 32 * hh) * 4);
-      f32x4 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool ok = rowok && kp0 + 32 * hh + 4 * j < len;
-        v[j] = ok ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, base + 16 * j, 0, 0))
-                  : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      const uint32_t base = (uint32_t)((((int64_t)ch.x0 + r) * a.AW + acol + kp0 + 32 * hh) * 2);
 #pragma unroll
       for (int pp = 0; pp < 4; ++pp) {
-        const f32x4 lo = v[2 * pp], hi = v[2 * pp + 1];
-        const uint4 pk = make_uint4(pack_bf2(__float_as_uint(lo.x), __float_as_uint(lo.y)),
-                                    pack_bf2(__float_as_uint(lo.z), __float_as_uint(lo.w)),
-                                    pack_bf2(__float_as_uint(hi.x), __float_as_uint(hi.y)),
-                                    pack_bf2(__float_as_uint(hi.z), __float_as_uint(hi.w)));
+        const bool ok = rowok && kp0 + 32 * hh + 8 * pp < len;
+        const u32x4 v = ok ? __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, base + 16 * pp, 0, 0))
+                           : u32x4{0u, 0u, 0u, 0u};
         const int pos = (4 * hh + pp) ^ ((r >> 1) & 7);
-        *reinterpret_cast<uint4*>(slot + r * PROW + 16 * pos) = pk;
+        *reinterpret_cast<u32x4*>(slot + r * PROW + 16 * pos) = v;
       }
     }
     if (!own) {
@@ -421,17 +427,24 @@ k_prefill_main(PfArgs a) {
 // ---------------------------------------------------------------------------
 
 struct PpArgs {
-  const uint16_t* x;         // [n][d_in]
-  const int32_t* perm;       // sorted position -> token
+  const uint16_t* x;            // [n][d_in]
+  const int32_t* perm;          // sorted position -> token
   const PfProItem* items;
-  const DecVeraRow* vrows;   // [32 nvb]
-  const uint16_t* A_sh;      // [r_v][d_in]
-  uint16_t* dx;              // [n_rot][d_in] Delta rows by sorted position
-  float* acc;                // [n][AW] shrink sums
-  int32_t d_in, AW, RT;
+  const DecVeraRow* vrows;      // [64 nvb]
+  const uint16_t* A_sh;         // [r_v][d_in]
+  uint16_t* dx;                 // [n_rot][d_in] Delta rows by sorted position
+  unsigned long long* acc;      // [n][AW] this forward's shrink sums (zero on entry)
+  unsigned long long* acc_next; // the other buffer, cleared for the next forward
+  uint16_t* tbf;                // [n][AW] finished sums in bf16
+  int32_t* tcnt;                // [shrink tiles] arrival counters
+  uint32_t acc_words;           // n AW
+  uint32_t acc_bytes, tbf_bytes;
+  int32_t KP;                   // K parts of a shrink tile
+  uint32_t x_bytes, ash_bytes;
+  int32_t d_in, AW, RT, r_v;
 };
 
-// Delta = x (R - I) for up to 32 rows and 1024 columns (64 per wave). With
+// Delta = x (R - I) for up to 32 rows and 256 columns (64 per wave). With
 // blocks of a multiple of 32, each 32-column MFMA block lies in one diagonal
 // block and takes blk / 16 k-steps: A = the rows' x over that block, B = the
 // block's (R - I)^T rows (stored transposed, so a column's k values are
@@ -493,16 +506,47 @@ __device__ void pp_rotate_scalar(const PpArgs& a, const PfProItem& it, int tid) 
   }
 }
 
-// 16 waves per item: a shrink tile's K slices of 256 (one per wave) meet in
-// LDS and four waves add them in slice order; a rotation item spreads its
-// 1024 columns over the waves.
-constexpr int PP_WAVES = 16;
-__global__ void __launch_bounds__(64 * PP_WAVES) k_prefill_prologue(PpArgs a) {
-  __shared__ f32x4 red[PP_WAVES][4][64];
-  const PfProItem it = a.items[blockIdx.x];
+// Shrink tile: 64 rows x 64 ranks over one K part of 1024, in 4 slices of
+// 256. Each slice's rows (gathered by token) and A rows land in LDS by direct
+// buffer->LDS loads (one instruction: 2 rows of 512 bytes; 16-byte piece p of
+// row r stored at position p ^ (r & 31), so the 32 rows an MFMA operand read
+// touches fall in distinct banks), two slices in flight in two buffers; wave
+// w multiplies row block w & 1 by rank block w >> 1. One atomic per output
+// and K part.
+constexpr int PP_ROW = 512;                  // bytes of a staged row (256 k)
+constexpr int PP_BUF = 2 * 64 * PP_ROW;      // 64 x rows, then 64 A rows
+constexpr int PP_LOADS = 16;                 // direct loads per wave and slice
+__device__ __forceinline__ uint4 pp_frag(const uint8_t* base, int r, int piece) {
+  return *reinterpret_cast<const uint4*>(base + r * PP_ROW + 16 * (piece ^ (r & 31)));
+}
+__device__ __forceinline__ void pp_stage(uint8_t* buf, rsrc_t rx, rsrc_t ra, const uint32_t (&xoff)[8],
+                                         const uint32_t (&aoff)[8], int soff, int w) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void*)(buf + (w + 4 * q) * 1024), 16, xoff[q], soff, 0, 0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(buf + 64 * PP_ROW + (w + 4 * q) * 1024), 16,
+                                             aoff[q], soff, 0, 0);
+}
+__device__ __forceinline__ void pp_mul(const uint8_t* buf, f32x16& acc, int rb, int cb, int m, int h) {
+#pragma unroll
+  for (int s = 0; s < 16; ++s)
+    acc = mfma32(pp_frag(buf, 32 * rb + m, 2 * s + h), pp_frag(buf + 64 * PP_ROW, 32 * cb + m, 2 * s + h), acc);
+}
+
+__global__ void __launch_bounds__(256) k_prefill_prologue(PpArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[PP_BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[PP_BUF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, h = lane >> 5;
+  {
+    f32x4* z = reinterpret_cast<f32x4*>(a.acc_next);
+    for (uint32_t i = blockIdx.x * 256 + tid; i < a.acc_words / 2; i += gridDim.x * 256)
+      z[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const PfProItem it = a.items[blockIdx.x];
   const int64_t d_in = a.d_in;
   if (it.type == PP_ROT) {
     if (it.blk % 32 == 0)
@@ -511,45 +555,111 @@ __global__ void __launch_bounds__(64 * PP_WAVES) k_prefill_prologue(PpArgs a) {
       pp_rotate_scalar(a, it, tid);
     return;
   }
-  // shrink tile of 32 rows x 32 ranks: wave w sums K slice w (d_in = 16 x 256)
-  const uint16_t* xr;
-  const uint16_t* ar;
-  if (it.type == PP_SHRINK) {
-    const int nk = it.k >> 16;
-    xr = a.x + (size_t)ldg(a.perm + it.p0 + min(m, it.n - 1)) * d_in;
-    ar = it.ptr + (size_t)((it.k & 0xFFFF) + min(m, nk - 1)) * d_in;
-  } else {
-    xr = a.x + (size_t)a.vrows[32 * it.p0 + m].tok * d_in;
-    ar = a.A_sh + (size_t)(32 * it.k + m) * d_in;
+  const bool vera = it.type == PP_VSHRINK;
+  const int k0 = it.k & 0xFFFF, nk = it.k >> 16;
+  const int kbase = it.blk * 1024;  // this item's K part
+  // (1) sources: this lane's row in each of its 8 x and 8 A instructions
+  //     (instruction j: rows 2 j, 2 j + 1)
+  const int pos = lane & 31;
+  uint32_t xoff[8], aoff[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = 2 * (w + 4 * q) + (lane >> 5);
+    const int tok = vera ? a.vrows[64 * it.p0 + r].tok : ldg(a.perm + it.p0 + min(r, it.n - 1));
+    xoff[q] = (uint32_t)(((int64_t)tok * d_in + 8 * (pos ^ (r & 31))) * 2);
+    aoff[q] = (uint32_t)(((int64_t)(k0 + min(r, nk - 1)) * d_in + 8 * (pos ^ (r & 31))) * 2);
   }
-  const int64_t koff = (int64_t)w * 256 + 32 * h;
-  const f32x16 acc = shrink_tile(xr + koff, ar + koff);
+  const rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+  const rsrc_t ra = vera ? make_rsrc(a.A_sh, a.ash_bytes)
+                         : make_rsrc(it.ptr, (uint32_t)((int64_t)(k0 + nk) * d_in * 2));
+  issue_fence();
+  pp_stage(buf0, rx, ra, xoff, aoff, kbase * 2, w);
+  pp_stage(buf1, rx, ra, xoff, aoff, (kbase + 256) * 2, w);
+  issue_fence();
+  // VeRA: rows and d of this lane's outputs, fetched while the loads land
+  const int rb = w & 1, cb = w >> 1;
+  int32_t prow[16];
+  float dsc[16];
+  if (vera) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) red[w][c][lane] = f32x4{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
-  lds_barrier();
-  if (w >= 4) return;
-  // wave c adds elements 4 c .. 4 c + 3 of every lane over the slices, in
-  // slice order, so every forward gives the same sums
-  const int c = w;
-  f32x4 sum = red[0][c][lane];
-#pragma unroll
-  for (int v = 1; v < PP_WAVES; ++v) sum += red[v][c][lane];
-  // element 4 c + e: row 8 c + 4 h + e of the tile, rank column m
-  if (it.type == PP_SHRINK) {
-    const int k0 = it.k & 0xFFFF, nk = it.k >> 16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = 8 * c + 4 * h + e;
-      if (row < it.n && m < nk) a.acc[(size_t)(it.p0 + row) * a.AW + k0 + m] = sum[e];
+    for (int i = 0; i < 16; ++i) {
+      const DecVeraRow o = a.vrows[64 * it.p0 + 32 * rb + 8 * (i >> 2) + 4 * h + (i & 3)];
+      prow[i] = o.p;
+      dsc[i] = ldg(o.vd + k0 + 32 * cb + m);
     }
-  } else {
-    // VeRA row 32 p0 + row, rank 32 k + m; d scales each rank (it commutes
-    // with the K sum)
-    const int j = 32 * it.k + m;
+  }
+  // (2) four slices, two buffers
+  f32x16 acc = {};
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+  wg_barrier();
+  pp_mul(buf0, acc, rb, cb, m, h);
+  wg_barrier();
+  pp_stage(buf0, rx, ra, xoff, aoff, (kbase + 512) * 2, w);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+  wg_barrier();
+  pp_mul(buf1, acc, rb, cb, m, h);
+  wg_barrier();
+  pp_stage(buf1, rx, ra, xoff, aoff, (kbase + 768) * 2, w);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+  wg_barrier();
+  pp_mul(buf0, acc, rb, cb, m, h);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  wg_barrier();
+  pp_mul(buf1, acc, rb, cb, m, h);
+  // (3) add the partial sums: element i is row 32 rb + 8 (i / 4) + 4 h + i % 4
+  //     of the tile, rank k0 + 32 cb + m
+  const int j = 32 * cb + m;
+  const int col = (vera ? a.RT : 0) + k0 + j;
+  if (j < nk) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const DecVeraRow o = a.vrows[32 * it.p0 + 8 * c + 4 * h + e];
-      if (o.p >= 0) a.acc[(size_t)o.p * a.AW + a.RT + j] = sum[e] * ldg(o.vd + j);
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * rb + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (vera) {
+        if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + col, fx_from(acc[i] * dsc[i]));
+      } else if (r < it.n) {
+        atomicAdd(a.acc + (size_t)(it.p0 + r) * a.AW + col, fx_from(acc[i]));
+      }
+    }
+  }
+  // (4) the last K part of the tile to arrive converts the tile's sums to
+  //     bf16 (the atomics have completed in memory before each part counts
+  //     its arrival; the sums are read past the caches)
+  __shared__ int32_t last_part;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  if (tid == 0) {
+    const int old = arrive(a.tcnt + it.pad);
+    last_part = old == a.KP - 1;
+    if (old == a.KP - 1) reset_counter(a.tcnt + it.pad);
+  }
+  lds_barrier();
+  if (!last_part) return;
+  {
+    // thread -> tile row tid / 4, ranks 16 (tid % 4) .. + 15
+    const int r = tid >> 2, c16 = 16 * (tid & 3);
+    int32_t row;
+    if (vera)
+      row = a.vrows[64 * it.p0 + r].p;
+    else
+      row = r < it.n ? it.p0 + r : -1;
+    if (row >= 0 && c16 < nk) {
+      const rsrc_t sr = make_rsrc(a.acc, a.acc_bytes);
+      const int cbase = (vera ? a.RT : 0) + k0 + c16;
+      const uint32_t off = (uint32_t)(((int64_t)row * a.AW + cbase) * 8);
+      f32x4 q[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[e] = ld_sys4(sr, off + 16 * e);
+      uint32_t wv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const u32x4 v = __builtin_bit_cast(u32x4, q[e]);
+        const float lo = fx_to((long long)(((unsigned long long)v.y << 32) | v.x));
+        const float hi = fx_to((long long)(((unsigned long long)v.w << 32) | v.z));
+        wv[e] = pack_bf2(__float_as_uint(lo), __float_as_uint(hi));
+      }
+      uint16_t* dst = a.tbf + (size_t)row * a.AW + cbase;
+      *(GLOBAL u32x4*)dst = u32x4{wv[0], wv[1], wv[2], wv[3]};
+      *(GLOBAL u32x4*)(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
     }
   }
 }
@@ -559,6 +669,10 @@ __global__ void __launch_bounds__(64 * PP_WAVES) k_prefill_prologue(PpArgs a) {
 scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                             float* y, hipStream_t st, int32_t* launches) {
   const PrefillPlan& P = B->pp;
+  // the shrink sums of this forward and the buffer cleared for the next
+  long long* acc = P.acc64[P.fwd & 1];
+  long long* acc_next = P.acc64[(P.fwd + 1) & 1];
+  ++P.fwd;
   int nl = 0;
   if (P.n_pro > 0) {
     PpArgs pa{};
@@ -568,12 +682,22 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
     pa.vrows = P.vrows;
     pa.A_sh = (const uint16_t*)L->A_sh;
     pa.dx = (uint16_t*)B->delta;
-    pa.acc = P.acc32;
+    pa.acc = (unsigned long long*)acc;
+    pa.acc_next = (unsigned long long*)acc_next;
+    pa.acc_words = P.acc_bytes / 8;
+    pa.acc_bytes = P.acc_bytes;
+    pa.tbf = P.tbf;
+    pa.tcnt = P.tcnt;
+    pa.tbf_bytes = P.tbf_bytes;
+    pa.KP = (int32_t)(L->d_in / 1024);
+    pa.x_bytes = (uint32_t)((size_t)B->n * L->d_in * 2);
+    pa.ash_bytes = (uint32_t)((size_t)L->r_v * L->d_in * 2);
     pa.d_in = (int32_t)L->d_in;
     pa.AW = P.AW;
     pa.RT = P.RT;
+    pa.r_v = L->r_v;
     ProfScope ps(L, st, "prefill_prologue");
-    hipLaunchKernelGGL(k_prefill_prologue, dim3(P.n_pro), dim3(64 * PP_WAVES), 0, st, pa);
+    hipLaunchKernelGGL(k_prefill_prologue, dim3(P.n_pro), dim3(256), 0, st, pa);
     ++nl;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch k_prefill_prologue");
@@ -585,9 +709,9 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
   ma.chunks = P.chunks;
   ma.crow = P.crow;
   ma.B_sh = (const uint16_t*)L->B_sh;
-  ma.acc = P.acc32;
+  ma.tbf = P.tbf;
   ma.y = y;
-  ma.acc_bytes = P.acc_bytes;
+  ma.acc_bytes = P.tbf_bytes;
   ma.x_bytes = (uint32_t)((size_t)B->n * L->d_in * 2);
   ma.dx_bytes = (uint32_t)((size_t)B->n_rot * L->d_in * 2);
   ma.d_in = (int32_t)L->d_in;

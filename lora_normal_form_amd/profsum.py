@@ -25,7 +25,7 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["csrc/decode.hip", "csrc/forward.hip", "csrc/prefill.hip"]
+KERNEL_SOURCES = ["csrc/decode.hip", "csrc/forward.hip", "csrc/prefill.hip", "csrc/kernels.h"]
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
