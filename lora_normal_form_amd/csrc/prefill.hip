@@ -724,6 +724,11 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
   ma.cnt = P.cnt;
   ma.part_bytes = P.part_bytes;
   ma.P = P.P;
+  // every table the kernel dereferences must be there
+  if (!ma.chunks || !ma.crow || !ma.items || !ma.x || !ma.W || !ma.y ||
+      (P.P > 1 && (!ma.part || !ma.cnt)) || (B->n_rot > 0 && !ma.dx) ||
+      (B->n_vera > 0 && !ma.B_sh) || (P.AW > 0 && !ma.tbf))
+    return fail(SCUTE_E_STATE, "prefill path: plan tables missing");
   {
     ProfScope ps(L, st, "prefill_main");
     hipLaunchKernelGGL(k_prefill_main<64>, dim3(P.n_items), dim3(256), 0, st, ma);
