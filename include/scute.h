@@ -184,7 +184,9 @@ scute_status scute_unload_adapter(scute_layer* layer, int32_t id, void* stream);
 scute_status scute_plan_batch(scute_layer* layer, const int32_t* token_adapter,
                               int32_t n, void* stream, scute_batch** out);
 
-/* Free a plan (after the streams that used it are synchronised). Null ok. */
+/* Free a plan (after the streams that used it are synchronised). Null ok.
+ * The plan records its device when it is built, so it may be freed before
+ * or after its layer. */
 scute_status scute_batch_destroy(scute_batch* batch);
 
 /* The forward pass on `stream` (null: default stream), asynchronous.

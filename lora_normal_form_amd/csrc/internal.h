@@ -218,7 +218,8 @@ struct PrefillPlan {
 }  // namespace scute
 
 struct scute_batch {
-  const scute_layer* layer = nullptr;
+  const scute_layer* layer = nullptr;  // compared only: the layer may be destroyed first
+  int32_t device = -1;                 // device of the allocations below (-1: none)
   uint64_t epoch = 0;
   int32_t n = 0;
   int32_t n_rot = 0;      // sorted positions [0, n_rot) carry a rotation

@@ -14,6 +14,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <thread>
 
@@ -218,6 +219,11 @@ extern "C" scute_status scute_layer_create(int32_t device, int64_t d_in, int64_t
       return fail(SCUTE_E_INVALID, "scute_layer_create: max_adapters must be in [1, 2^20]");
     if (device < -1) return fail(SCUTE_E_INVALID, "scute_layer_create: device must be >= -1");
     auto* L = new scute_layer();
+    // every layer starts its epochs in a range of its own, so a plan kept past
+    // its layer's destruction never passes the staleness check of a new layer
+    // allocated at the same address
+    static std::atomic<uint64_t> serial{0};
+    L->epoch = (serial.fetch_add(1) + 1) << 32;
     L->device = device;
     L->d_in = d_in;
     L->d_out = d_out;

@@ -32,7 +32,7 @@ int row_class(const SlotEntry& E) {
 }
 
 void free_batch_memory(scute_batch* B) {
-  int dev = B->layer ? B->layer->device : -1;
+  const int dev = B->device;
   if (dev >= 0) {
     int prev = -1;
     (void)hipGetDevice(&prev);
@@ -66,6 +66,7 @@ extern "C" scute_status scute_plan_batch(scute_layer* L, const int32_t* token_ad
     }
     auto* B = new scute_batch();
     B->layer = L;
+    B->device = L->device;
     B->epoch = L->epoch;
     B->n = n;
     B->perm.resize(n);

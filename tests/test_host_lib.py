@@ -260,3 +260,20 @@ def test_error_paths_leave_layer_usable():
     assert _err(scute.scute_read_slot, L.h, 1, scute.SLOT_S, 3) == scute.E_SHAPE
     assert _err(scute.scute_set_vera_shared, L.h, 16, 32, 0) == scute.E_SHAPE
     assert _err(scute.scute_set_vera_shared, L.h, 17, 32, 3) == scute.E_INVALID  # misaligned
+
+
+def test_plan_outlives_its_layer():
+    # a plan may be freed after its layer (finalisers of objects caught in a
+    # reference cycle run in any order); a layer created afterwards, possibly
+    # at the same address, rejects the old plan instead of using it
+    for _ in range(8):
+        L1 = scute.Layer(32, 16, "f32", max_adapters=2, device=-1)
+        L1.load(0, "lora", rank=2, A=np.ones((2, 32)), B=np.ones((16, 2)))
+        b = L1.plan([0, -1, 0])
+        L1.close()
+        L2 = scute.Layer(32, 16, "f32", max_adapters=2, device=-1)
+        L2.load(0, "lora", rank=2, A=np.ones((2, 32)), B=np.ones((16, 2)))
+        assert _err(scute.scute_cost_model, L2.h, b.h) == scute.E_STATE
+        b.close()
+        assert L2.cost(L2.plan([0, 0]))["bytes"] > 0
+        L2.close()

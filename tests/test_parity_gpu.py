@@ -170,3 +170,18 @@ def test_empty_batch_and_errors_on_device():
         ld.layer.forward(ld.batch, ld.x, ld.W, ld.y)
     assert e.value.code == scute.E_STATE
     torch.cuda.synchronize()
+
+
+def test_plan_freed_after_its_layer():
+    # the plan records its device: freeing it after the layer touches no
+    # freed layer memory and leaves no HIP error behind for the next launch
+    _need_gpu()
+    from lora_normal_form_amd import workload as glue
+    wl = _small("bf16", ALL_METHODS, [0, 1, 2], seed=8)
+    ld = glue.load(wl, device=0)
+    ld.layer.close()
+    ld.batch.close()
+    t = torch.zeros(1024, device="cuda:0")
+    t.fill_(1.0)
+    torch.cuda.synchronize()
+    assert float(t.sum()) == 1024.0
