@@ -208,15 +208,14 @@ struct MainArgs {
   const uint16_t* xs;               // [32 MGT][d_in] sorted x rows, then delta rows
   const uint16_t* W;
   const DecRow* rows;               // [M_pad]
-  const int4* items;                // expand items by slice, own then VeRA
-  const uint16_t* const* item_ptr;  // per item: B' of its adapter (own) or B_sh (VeRA)
+  const DecStep* steps;             // expand steps by slice and K half
   const float* acc;                 // [M_pad][AW] shrink sums: RT own ranks, then r_v VeRA ranks
   const float* zeros;               // [d_out]
   float* part;                      // [S][C][M_pad][64] split-K partial tiles (S > 1)
   int32_t* cnt;                     // [C] arrival counters, kept at zero between forwards
   float* y;
   uint32_t acc_bytes, part_bytes;
-  int32_t off[9];                   // [2 S + 1]: slice k own items [2k, 2k+1), VeRA [2k+1, 2k+2)
+  int32_t off[9];                   // [2 S + 1]: slice k, K half h: steps [2k + h, 2k + h + 1)
   int32_t g_rot, d_in, d_out, k_chunk, S, C, RT, AW;
 };
 
@@ -329,73 +328,88 @@ __device__ __forceinline__ void ksteps_static(const WSrc& wrow, const uint16_t* 
   }
 }
 
-// Operands of up to 4 expand items of one kind (up to four 16-rank MFMA
-// steps each) for one wave: A = the rows' shrink sums (row 32 g + m of the
-// item's group, fp32 rounded to bf16), B = B' or B_sh rows of this lane's
-// column. Loads go through buffer resources, so ranks past a row's length
-// never read past the operand. The descriptors are fetched first (early, so
-// they are in registers when the operands are needed).
-struct ExpDesc {
-  int4 itm[4];
-  const uint16_t* bp[4];
+// Expand steps of one wave, 64 at a time: lane j holds the descriptor of
+// step base + j (zeros past the list), read by every lane with readlane.
+struct StepWin {
+  u32x4 d;
+  uint32_t plo, phi;
+  int base;
 };
-struct ExpBatch {
-  uint4 av[4][4], bv[4][4];
-  int32_t gi[4];
-};
-
-
-__device__ __forceinline__ void fetch_desc(const MainArgs& a, ExpDesc& d, int ib, int i1) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int it = min(ib + q, i1 - 1);
-    d.itm[q] = a.items[it];
-    d.bp[q] = a.item_ptr[it];
+__device__ __forceinline__ void load_win(const DecStep* steps, StepWin& w, int base, int end,
+                                         int lane) {
+  w.base = base;
+  w.d = u32x4{0u, 0u, 0u, 0u};
+  w.plo = w.phi = 0u;
+  if (base + lane < end) {
+    const GLOBAL u32x4* p = (const GLOBAL u32x4*)(steps + base + lane);
+    w.d = p[0];
+    const u32x4 q = p[1];
+    w.plo = q.x;
+    w.phi = q.y;
   }
 }
+struct StepDesc {
+  int gk, kk, rank, lo, hi;
+  const uint16_t* bp;
+};
+__device__ __forceinline__ StepDesc step_at(const StepWin& w, int j) {
+  StepDesc d;
+  d.gk = __builtin_amdgcn_readlane((int)w.d.x, j);
+  d.kk = __builtin_amdgcn_readlane((int)w.d.y, j);
+  d.rank = __builtin_amdgcn_readlane((int)w.d.z, j);
+  const int lohi = __builtin_amdgcn_readlane((int)w.d.w, j);
+  d.lo = lohi & 0xFFFF;
+  d.hi = lohi >> 16;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)w.plo, j);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)w.phi, j);
+  d.bp = (const uint16_t*)(((uint64_t)hi << 32) | lo);
+  return d;
+}
 
-__device__ __forceinline__ void load_operands(const MainArgs& a, const ExpDesc& d, ExpBatch& eb,
-                                              int ib, int i1, int kind, int64_t ncol, int m,
-                                              int h) {
+// A batch of up to NSL steps: raw operands as loaded (A: the row's 8 fp32
+// shrink sums of the lane's k half; B: 8 bf16 of the lane's column of B' or
+// B_sh), then the MFMA operands (A rounded to bf16; rows outside the step's
+// [lo, hi) and ranks past the term's rank zeroed). Loads go through buffer
+// resources, so nothing past an operand is read.
+constexpr int NSL = 8;
+struct RawBatch {
+  uint4 b[NSL], a0[NSL], a1[NSL];
+};
+struct OpBatch {
+  uint4 a[NSL], b[NSL];
+};
+__device__ __forceinline__ void issue_batch(const MainArgs& a, const StepWin& w, int s0, int nb,
+                                            RawBatch& rb, int64_t ncol, int m, int h) {
   const rsrc_t ar = make_rsrc(a.acc, a.acc_bytes);
-  const int32_t acol = kind == EXP_OWN ? 0 : a.RT;
-  // all loads first, conversions after, so the batch costs one round trip
-  uint4 braw[4][4], araw[4][4][2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int gi = uni(d.itm[q].x) >> 8;
-    const int k0 = uni(d.itm[q].y), rank = uni(d.itm[q].z) >> 8;
-    const int pa = 32 * gi + m;
-    const rsrc_t br = make_rsrc(uni_ptr(d.bp[q]), (uint32_t)(a.d_out * rank * 2));
-    const int nstp = (ib + q < i1) ? uni(d.itm[q].z) & 0xFF : 0;  // steps this item uses
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      if (st < nstp) {
-        const int kk = k0 + 16 * st + 8 * h;
-        braw[q][st] = ldb16(br, (uint32_t)((ncol * rank + kk) * 2));
-        const uint32_t ao = (uint32_t)(((int64_t)pa * a.AW + acol + kk) * 4);
-        araw[q][st][0] = ldb16(ar, ao);
-        araw[q][st][1] = ldb16(ar, ao + 16);
-      }
+  for (int j = 0; j < NSL; ++j) {
+    if (j < nb) {
+      const StepDesc d = step_at(w, s0 - w.base + j);
+      const int gi = d.gk >> 8;
+      const int kk = d.kk + 8 * h;  // the lane's first rank
+      const int acol = (d.gk & STEP_VERA) ? a.RT : 0;
+      const rsrc_t br = make_rsrc(d.bp, (uint32_t)(a.d_out * d.rank * 2));
+      rb.b[j] = ldb16(br, (uint32_t)((ncol * d.rank + kk) * 2));
+      const uint32_t ao = (uint32_t)(((int64_t)(32 * gi + m) * a.AW + acol + kk) * 4);
+      rb.a0[j] = ldb16(ar, ao);
+      rb.a1[j] = ldb16(ar, ao + 16);
     }
   }
+}
+__device__ __forceinline__ void convert_batch(const StepWin& w, int s0, int nb, const RawBatch& rb,
+                                              OpBatch& ob, int m, int h) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int gi = uni(d.itm[q].x) >> 8;
-    const int k0 = uni(d.itm[q].y), nstp = uni(d.itm[q].z) & 0xFF, rank = uni(d.itm[q].z) >> 8;
-    const int lo = uni(d.itm[q].w) & 0xFFFF, hi = uni(d.itm[q].w) >> 16;
-    const int pa = 32 * gi + m;
-    const bool rowok = (ib + q < i1) && pa >= lo && pa < hi;
-    eb.gi[q] = gi;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kk = k0 + 16 * st + 8 * h;
-      const bool ok = st < nstp && kk < rank;
-      const uint4 a0 = araw[q][st][0], a1 = araw[q][st][1];
+  for (int j = 0; j < NSL; ++j) {
+    if (j < nb) {
+      const StepDesc d = step_at(w, s0 - w.base + j);
+      const int pa = 32 * (d.gk >> 8) + m;
+      const bool ok = d.kk + 8 * h < d.rank;
+      const bool rowok = pa >= d.lo && pa < d.hi;
+      const uint4 a0 = rb.a0[j], a1 = rb.a1[j];
       const uint4 av = make_uint4(pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w),
                                   pack_bf2(a1.x, a1.y), pack_bf2(a1.z, a1.w));
-      eb.bv[q][st] = ok ? braw[q][st] : make_uint4(0, 0, 0, 0);
-      eb.av[q][st] = (ok && rowok) ? av : make_uint4(0, 0, 0, 0);
+      ob.b[j] = ok ? rb.b[j] : make_uint4(0, 0, 0, 0);
+      ob.a[j] = (ok && rowok) ? av : make_uint4(0, 0, 0, 0);
     }
   }
 }
@@ -473,18 +487,16 @@ k_decode_main(MainArgs a) {
   }
   stage_rows<MGT>(slot0 + kp * Cfg::STAGE, src, 0, cb);
   if constexpr (pre1) stage_rows<MGT>(slot1 + kp * Cfg::STAGE, src, (int64_t)SK * min(1, nst - 1), cb);
-  // (3) this wave's expand items (waves kp = 0: own items, kp = 1: VeRA
-  //     items); their descriptors load now and are used after the K loop
-  const int kind = kp;
+  // (3) this wave's expand steps (its K half's share of the slice's items);
+  //     the first 64 descriptors load now and are used after the K loop
   int i0 = 0, i1 = 0;
 #pragma unroll
   for (int i = 0; i < 9; ++i) {
-    if (i == 2 * kc + kind) i0 = a.off[i];
-    if (i == 2 * kc + kind + 1) i1 = a.off[i];
+    if (i == 2 * kc + kp) i0 = a.off[i];
+    if (i == 2 * kc + kp + 1) i1 = a.off[i];
   }
-  ExpDesc ed;
-  if (i0 < i1) fetch_desc(a, ed, i0, i1);
-  ExpBatch eb;
+  StepWin win;
+  load_win(a.steps, win, i0, i1, lane);
 
   f32x16 acc[MGT];
 #pragma unroll
@@ -535,7 +547,8 @@ k_decode_main(MainArgs a) {
   // ---- epilogue ---------------------------------------------------------------
   // the first expand batch's operands and the rows' factor vectors are in
   // flight while the K halves meet
-  if (i0 < i1) load_operands(a, ed, eb, i0, i1, kind, ncol, m, h);
+  RawBatch rb;
+  if (i0 < i1) issue_batch(a, win, i0, min(NSL, i1 - i0), rb, ncol, m, h);
   const int q4 = tid & 15, rr = tid >> 4;  // float4 of the row, row within 16
   const int nj = 2 * mgx;                  // passes of 16 rows over the x rows
   const int64_t cbase = (int64_t)c * 64 + 4 * q4;
@@ -589,28 +602,29 @@ k_decode_main(MainArgs a) {
   }
   wg_barrier();
 
-  // (c) expand: own items add t B' into T; VeRA items of one row group sum
-  //     into one fragment that goes to V
+  // (c) expand: batches of NSL steps, the next batch's operands loading
+  //     while this one multiplies. Own steps sum one item's product in
+  //     registers and add it into T on the rows of its segment; VeRA steps
+  //     of one row group sum into one fragment that goes to V. The two K-half
+  //     waves of a column block hold disjoint segments and groups.
   {
     int cg = -1;
-    f32x16 vacc = {};
-    for (int ib = i0; ib < i1; ib += 4) {
-      if (ib != i0) {
-        fetch_desc(a, ed, ib, i1);
-        load_operands(a, ed, eb, ib, i1, kind, ncol, m, h);
-      }
+    f32x16 t2 = {}, vacc = {};
+    for (int sc = i0; sc < i1;) {
+      const int nb = min(NSL, i1 - sc);
+      OpBatch ob;
+      convert_batch(win, sc, nb, rb, ob, m, h);
+      const int sn = sc + nb;
+      // the next batch stays in this window (batches start at i0 + NSL t and
+      // a window holds 64 / NSL of them)
+      const bool same_win = sn < i1 && sn + min(NSL, i1 - sn) <= win.base + 64;
+      if (same_win) issue_batch(a, win, sn, min(NSL, i1 - sn), rb, ncol, m, h);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (ib + q >= i1) continue;
-        f32x16 t2 = {};
-#pragma unroll
-        for (int st = 0; st < 4; ++st) t2 = mfma32(eb.av[q][st], eb.bv[q][st], t2);
-        const int gi = eb.gi[q];
-        if (kind == EXP_OWN) {
-          float* Tg = T + 32 * gi * 64 + cb * 32 + m;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] += t2[i];
-        } else {
+      for (int j = 0; j < NSL; ++j) {
+        if (j >= nb) continue;
+        const StepDesc d = step_at(win, sc - win.base + j);
+        const int gi = d.gk >> 8;
+        if (d.gk & STEP_VERA) {
           if (gi != cg) {
             if (cg >= 0) {
               float* Vg = V + 32 * cg * 64 + cb * 32 + m;
@@ -619,12 +633,27 @@ k_decode_main(MainArgs a) {
               if (lane == 0) vflag[cg] = 1;
             }
             cg = gi;
-            vacc = t2;
-          } else {
-            vacc += t2;
+            vacc = f32x16{};
+          }
+          vacc = mfma32(ob.a[j], ob.b[j], vacc);
+        } else {
+          t2 = mfma32(ob.a[j], ob.b[j], t2);
+          if (d.gk & STEP_LAST) {
+            float* Tg = T + 32 * gi * 64 + cb * 32 + m;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+              if (32 * gi + r >= d.lo && 32 * gi + r < d.hi) Tg[r * 64] += t2[i];
+            }
+            t2 = f32x16{};
           }
         }
       }
+      if (sn < i1 && !same_win) {
+        load_win(a.steps, win, sn, i1, lane);
+        issue_batch(a, win, sn, min(NSL, i1 - sn), rb, ncol, m, h);
+      }
+      sc = sn;
     }
     if (cg >= 0) {
       float* Vg = V + 32 * cg * 64 + cb * 32 + m;
@@ -754,8 +783,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.xs = D.xs;
   ma.W = (const uint16_t*)W;
   ma.rows = D.rows;
-  ma.items = D.exp_items;
-  ma.item_ptr = D.exp_ptr;
+  ma.steps = D.steps;
   ma.acc = acc;
   ma.zeros = D.zeros;
   ma.part = D.part;
@@ -763,7 +791,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.y = y;
   ma.acc_bytes = D.acc_bytes;
   ma.part_bytes = D.part_bytes;
-  for (int i = 0; i < 9; ++i) ma.off[i] = D.exp_off[i];
+  for (int i = 0; i < 9; ++i) ma.off[i] = D.step_off[i];
   ma.g_rot = D.g_rot;
   ma.d_in = (int32_t)L->d_in;
   ma.d_out = (int32_t)L->d_out;

@@ -101,13 +101,24 @@ struct DecRow {
 //   VeRA shrink: p0 = block of 32 VeRA rows, n = block of 32 ranks,
 //                k = K slice (256 wide)
 enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3 };
-// expand item kinds of the decode main kernel
-enum : int32_t { EXP_OWN = 0, EXP_VERA = 1 };
+// One 16-rank step of the decode main kernel's expand: an MFMA step over
+// ranks [kk, kk + 16) of one row group's own term (t B' against the
+// adapter's B') or shared VeRA term (u B_sh). 32 bytes.
+//   gk   kind (STEP_VERA) | STEP_LAST on an own item's last step | group << 8
+//   kk   first rank of the step; rank = length of a B row (the term's rank)
+//   lohi sorted rows [lo, hi) of the group the step contributes to
+//   bp   B' of the adapter, or B_sh
+enum : int32_t { STEP_VERA = 1, STEP_LAST = 2 };
+struct DecStep {
+  int32_t gk, kk, rank, lohi;
+  const uint16_t* bp;
+  int64_t pad;
+};
 struct DecProItem {
   int32_t type, p0, n, k;
   int32_t tok[4];
   const uint16_t* ptr;
-  int32_t blk, grp;
+  int32_t blk, pad;
 };
 
 // VeRA row of a decode batch: d of its adapter, its token and sorted
@@ -129,13 +140,13 @@ struct DecodePlan {
   int32_t C = 0;        // column tiles of 64 outputs
   int32_t k_chunk = 0;  // d_in / S
   int32_t n_pro = 0;    // prologue work items
-  int32_t n_exp = 0;
-  int32_t exp_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};  // [2 S + 1] expand items by slice and kind
+  int32_t n_steps = 0;
+  // [2 S + 1]: the expand steps of slice k's K half h are [2k + h, 2k + h + 1)
+  int32_t step_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
   const DecRow* rows = nullptr;          // [M_pad]
   const DecProItem* pro_items = nullptr; // [n_pro]
   const DecVeraRow* vrows = nullptr;     // [32 nvb]
-  const int4* exp_items = nullptr;       // expand items by slice, own then VeRA
-  const uint16_t* const* exp_ptr = nullptr;  // per expand item: B' or B_sh
+  const DecStep* steps = nullptr;        // [n_steps]
   const float* zeros = nullptr;          // [d_out] of 0.0f
   uint16_t* xs = nullptr;     // [M_pad + 32 g_rot][d_in] bf16: sorted x rows, then delta rows
   float* acc32[2] = {nullptr, nullptr};  // per parity: [M_pad][AW] fp32 shrink sums

@@ -11,8 +11,9 @@
 // MFMA steps:
 //   own item   (row group g, adapter segment, 64 ranks) against B'
 //   VeRA item  (row group g, 64 ranks) against the shared B_sh
-// Each K slice of a tile takes a share of both kinds; own items run on the
-// tile's first two waves, VeRA items on the other two.
+// Each K slice of a tile takes a share of both kinds, split between its two
+// K-half waves of each column block, and every item becomes a list of 16-rank
+// steps that the wave walks in batches.
 // The prologue items (gather of the sorted x rows, rotation, own-term
 // shrink, VeRA shrink) are listed here too, with every pointer and token
 // resolved; see decode.hip for the kernels.
@@ -97,13 +98,13 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const int32_t n_pro = n_gather + n_rot_items + KQ * n_sgroups + SV * nvb * njb;
   D.AW = D.RT + (B->n_vera > 0 ? L->r_v : 0);
 
-  // ---- expand items ----------------------------------------------------------
-  // item: (type | row group << 8, first rank, 16-rank steps (<= 4) | B row
-  // length << 8, first row | end row << 16), plus the B pointer
+  // ---- expand steps -----------------------------------------------------------
+  // item: the steps of one row group's term over up to 64 ranks (own: one
+  // adapter segment's rows of the group against its B'; VeRA: the group's
+  // VeRA rows against B_sh)
   struct Item {
-    int4 v;
+    int32_t g, kind, k, nst, rank, lo, hi;
     const uint16_t* ptr;
-    int32_t cost;
   };
   std::vector<Item> own_items, vera_items;
   std::vector<int32_t> row_vera(D.M_pad, 0);
@@ -117,11 +118,9 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     if (!(E.flags & F_TERM)) continue;
     for (int32_t g = start / 32; g * 32 < start + len; ++g) {
       const int32_t lo = std::max(start, 32 * g), hi = std::min(start + len, 32 * g + 32);
-      for (int32_t k = 0; k < E.rank; k += 64) {
-        const int32_t nst = std::min(4, (E.rank - k + 15) / 16);
-        own_items.push_back({make_int4(EXP_OWN | (g << 8), k, nst | (E.rank << 8), lo | (hi << 16)),
-                             (const uint16_t*)E.B, nst});
-      }
+      for (int32_t k = 0; k < E.rank; k += 64)
+        own_items.push_back({g, 0, k, std::min(4, (E.rank - k + 15) / 16), E.rank, lo, hi,
+                             (const uint16_t*)E.B});
     }
   }
   if (B->n_vera > 0) {
@@ -129,50 +128,89 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
       bool any = false;
       for (int32_t p = 32 * g; p < std::min(n, 32 * g + 32); ++p) any |= row_vera[p] != 0;
       if (!any) continue;
-      for (int32_t k = 0; k < L->r_v; k += 64) {
-        const int32_t nst = std::min(4, (L->r_v - k) / 16);
-        vera_items.push_back({make_int4(EXP_VERA | (g << 8), k, nst | (L->r_v << 8),
-                                        (32 * g) | ((32 * g + 32) << 16)),
-                              (const uint16_t*)L->B_sh, nst});
-      }
+      for (int32_t k = 0; k < L->r_v; k += 64)
+        vera_items.push_back({g, STEP_VERA, k, std::min(4, (L->r_v - k) / 16), L->r_v, 32 * g,
+                              32 * g + 32, (const uint16_t*)L->B_sh});
     }
   }
-  // spread each kind over the S slices (greedy by cost); VeRA items of a
-  // slice stay ordered by row group so one wave sums a group's items before
-  // storing it
-  auto spread = [&](std::vector<Item>& items, bool by_group) {
+  // spread each kind over the S slices (greedy by steps)
+  auto spread = [&](std::vector<Item>& items) {
     std::stable_sort(items.begin(), items.end(),
-                     [](const Item& p, const Item& q) { return p.cost > q.cost; });
+                     [](const Item& p, const Item& q) { return p.nst > q.nst; });
     std::vector<std::vector<Item>> per(S);
     std::vector<int64_t> load(S, 0);
     for (const Item& it : items) {
       const int32_t best = (int32_t)(std::min_element(load.begin(), load.end()) - load.begin());
       per[best].push_back(it);
-      load[best] += it.cost;
+      load[best] += it.nst;
     }
-    if (by_group)
-      for (auto& v : per)
-        std::stable_sort(v.begin(), v.end(),
-                         [](const Item& p, const Item& q) { return (p.v.x >> 8) < (q.v.x >> 8); });
     return per;
   };
-  const auto own_per = spread(own_items, false), vera_per = spread(vera_items, true);
-  std::vector<int4> exp;
-  std::vector<const uint16_t*> exp_ptr;
+  const auto own_per = spread(own_items), vera_per = spread(vera_items);
+  // Within a slice the two K-half waves of a column block share the expand.
+  // A unit (an own term's items of one adapter segment in one group, or a
+  // group's VeRA items) goes to one wave whole, so the two waves write
+  // disjoint rows of the row tile (own) and disjoint groups of the VeRA tile;
+  // units go to the wave with fewer steps so far, largest first. Each wave's
+  // VeRA steps are ordered by group (one group's products sum in registers).
+  std::vector<DecStep> steps;
   for (int32_t k = 0; k < S; ++k) {
-    D.exp_off[2 * k] = (int32_t)exp.size();
-    for (const Item& it : own_per[k]) {
-      exp.push_back(it.v);
-      exp_ptr.push_back(it.ptr);
+    std::vector<std::vector<Item>> units;
+    {
+      std::vector<Item> own(own_per[k]);
+      std::stable_sort(own.begin(), own.end(), [](const Item& p, const Item& q) {
+        return p.lo != q.lo ? p.lo < q.lo : p.k < q.k;
+      });
+      for (const Item& it : own) {
+        if (units.empty() || units.back()[0].kind != 0 || units.back()[0].lo != it.lo ||
+            units.back()[0].hi != it.hi || units.back()[0].ptr != it.ptr)
+          units.push_back({});
+        units.back().push_back(it);
+      }
+      std::vector<Item> vera(vera_per[k]);
+      std::stable_sort(vera.begin(), vera.end(), [](const Item& p, const Item& q) {
+        return p.g != q.g ? p.g < q.g : p.k < q.k;
+      });
+      for (const Item& it : vera) {
+        if (units.empty() || units.back()[0].kind != STEP_VERA || units.back()[0].g != it.g)
+          units.push_back({});
+        units.back().push_back(it);
+      }
     }
-    D.exp_off[2 * k + 1] = (int32_t)exp.size();
-    for (const Item& it : vera_per[k]) {
-      exp.push_back(it.v);
-      exp_ptr.push_back(it.ptr);
+    std::vector<int32_t> ord(units.size());
+    std::vector<int64_t> cost(units.size(), 0);
+    for (size_t u = 0; u < units.size(); ++u) {
+      ord[u] = (int32_t)u;
+      for (const Item& it : units[u]) cost[u] += it.nst;
+    }
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t p, int32_t q) { return cost[p] > cost[q]; });
+    std::vector<int32_t> half(units.size(), 0);
+    int64_t load[2] = {0, 0};
+    for (int32_t u : ord) {
+      half[u] = load[1] < load[0] ? 1 : 0;
+      load[half[u]] += cost[u];
+    }
+    for (int32_t hh = 0; hh < 2; ++hh) {
+      D.step_off[2 * k + hh] = (int32_t)steps.size();
+      // own units first, then VeRA units in group order (units are built in
+      // that order)
+      for (size_t u = 0; u < units.size(); ++u) {
+        if (half[u] != hh) continue;
+        for (const Item& it : units[u])
+          for (int32_t st = 0; st < it.nst; ++st) {
+            DecStep d{};
+            d.gk = it.kind | (it.kind == 0 && st == it.nst - 1 ? STEP_LAST : 0) | (it.g << 8);
+            d.kk = it.k + 16 * st;
+            d.rank = it.rank;
+            d.lohi = it.lo | (it.hi << 16);
+            d.bp = it.ptr;
+            steps.push_back(d);
+          }
+      }
     }
   }
-  D.exp_off[2 * S] = (int32_t)exp.size();
-  D.n_exp = (int32_t)exp.size();
+  D.step_off[2 * S] = (int32_t)steps.size();
+  D.n_steps = (int32_t)steps.size();
 
   // ---- one device allocation: tables, then zeroed workspaces -------------------
   size_t o = 0;
@@ -184,8 +222,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const size_t o_rows = take(sizeof(DecRow) * (size_t)D.M_pad);
   const size_t o_pro = take(sizeof(DecProItem) * (size_t)n_pro + 16);
   const size_t o_vrows = take(sizeof(DecVeraRow) * 32 * (size_t)nvb + 16);
-  const size_t o_exp = take(16 * exp.size() + 16);
-  const size_t o_ptr = take(8 * exp_ptr.size() + 8);
+  const size_t o_steps = take(sizeof(DecStep) * steps.size() + 16);
   const size_t o_ones = take(4 * (size_t)d_out);
   const size_t tables = o;
   const size_t o_zeros = take(4 * (size_t)d_out);
@@ -263,7 +300,6 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
           it.k = k | (std::min(4, E.rank - k) << 16);
           toks(it);
           it.ptr = (const uint16_t*)E.A;
-          it.grp = (int32_t)shrink_groups.size();
           shrink_groups.push_back(it);
         }
   }
@@ -310,8 +346,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   memcpy(h.data() + o_rows, rows.data(), sizeof(DecRow) * rows.size());
   if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), sizeof(DecProItem) * pro.size());
   if (!vrows.empty()) memcpy(h.data() + o_vrows, vrows.data(), sizeof(DecVeraRow) * vrows.size());
-  if (!exp.empty()) memcpy(h.data() + o_exp, exp.data(), 16 * exp.size());
-  if (!exp_ptr.empty()) memcpy(h.data() + o_ptr, exp_ptr.data(), 8 * exp_ptr.size());
+  if (!steps.empty()) memcpy(h.data() + o_steps, steps.data(), sizeof(DecStep) * steps.size());
   for (int64_t j = 0; j < d_out; ++j) {
     const float one = 1.0f;
     memcpy(h.data() + o_ones + 4 * j, &one, 4);
@@ -332,8 +367,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   D.rows = (const DecRow*)(d + o_rows);
   D.pro_items = (const DecProItem*)(d + o_pro);
   D.vrows = B->n_vera ? (const DecVeraRow*)(d + o_vrows) : nullptr;
-  D.exp_items = (const int4*)(d + o_exp);
-  D.exp_ptr = (const uint16_t* const*)(d + o_ptr);
+  D.steps = (const DecStep*)(d + o_steps);
   D.zeros = zeros;
   D.xs = (uint16_t*)(d + o_xs);
   D.acc32[0] = (float*)(d + o_acc0);
