@@ -114,6 +114,26 @@ __device__ __forceinline__ void pf_stage(uint8_t* slot, const PfSrc& src, int st
 }
 constexpr int PF_LOADS = 12;  // direct-to-LDS loads per wave and stage
 
+// Loads 3 P .. 3 P + 2 of a stage (the 4 row pieces, then the 8 W pieces),
+// so a wave can spread the next stage's loads over its MFMA steps instead of
+// waiting to issue all of them before it multiplies.
+template <int P>
+__device__ __forceinline__ void pf_stage_part(uint8_t* slot, const PfSrc& src, int stage, int w) {
+  const int soff = src.kb + stage * PK * 2;
+#pragma unroll
+  for (int i = 3 * P; i < 3 * P + 3; ++i) {
+    if (i < 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(i >= 2 ? src.rhi : src.rlo,
+                                               (lds_void*)(slot + (w + 4 * i) * 1024), 16,
+                                               src.roff[i], soff, 0, 0);
+    } else {
+      const int q = i - 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rw, (lds_void*)(slot + PSTAGE_X + (w + 4 * q) * 1024),
+                                               16, src.woff, soff + q * (int)src.wstep, 0, 0);
+    }
+  }
+}
+
 // MFMA operand of step s (k = 32 h + 8 s .. + 7 of the stage, the same
 // permutation of k on both operands) for staged row r
 __device__ __forceinline__ uint4 pf_frag(const uint8_t* base, int r, int s, int h) {
@@ -141,19 +161,31 @@ __device__ __forceinline__ void pf_mul(const uint4 (&av)[4], const uint4 (&bv)[2
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[g][cb] = mfma32(av[g], bv[cb], acc[g][cb]);
 }
+// With LD, a quarter of stage ns's loads (into slot nxt) goes out before each
+// k-step's MFMAs.
+template <bool LD>
 __device__ __forceinline__ void pf_mma(const uint8_t* slot, f32x16 (&acc)[4][2], int m, int h,
-                                       int w) {
+                                       int w, uint8_t* nxt = nullptr, const PfSrc* src = nullptr,
+                                       int ns = 0) {
   uint4 av[4][4], bv[4][2];
   pf_read(av[0], bv[0], slot, 0, m, h, w);
   pf_read(av[1], bv[1], slot, 1, m, h, w);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LD) pf_stage_part<0>(nxt, *src, ns, w);
+  __builtin_amdgcn_sched_barrier(0);
   pf_mul(av[0], bv[0], acc);
   pf_read(av[2], bv[2], slot, 2, m, h, w);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LD) pf_stage_part<1>(nxt, *src, ns, w);
   __builtin_amdgcn_sched_barrier(0);
   pf_mul(av[1], bv[1], acc);
   pf_read(av[3], bv[3], slot, 3, m, h, w);
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LD) pf_stage_part<2>(nxt, *src, ns, w);
+  __builtin_amdgcn_sched_barrier(0);
   pf_mul(av[2], bv[2], acc);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (LD) pf_stage_part<3>(nxt, *src, ns, w);
   __builtin_amdgcn_sched_barrier(0);
   pf_mul(av[3], bv[3], acc);
 }
@@ -171,8 +203,10 @@ __device__ __forceinline__ void pf_steps(const PfSrc& src, uint8_t* s0, uint8_t*
     uint8_t* nxt = TN % 3 == 0 ? s0 : (TN % 3 == 1 ? s1 : s2);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(T + 1 < NST ? PF_LOADS : 0));
     wg_barrier();
-    if constexpr (TN < NST) pf_stage(nxt, src, TN, w);
-    pf_mma(cur, acc, m, h, w);
+    if constexpr (TN < NST)
+      pf_mma<true>(cur, acc, m, h, w, nxt, &src, TN);
+    else
+      pf_mma<false>(cur, acc, m, h, w);
     pf_steps<NST, T + 1>(src, s0, s1, s2, acc, m, h, w);
   }
 }
