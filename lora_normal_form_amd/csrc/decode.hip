@@ -85,6 +85,34 @@ k_decode_prologue(ProArgs a) {
       z[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   for (int it = blockIdx.x; it < a.n_items; it += gridDim.x) {
+    if (it < a.n_vitems) {
+      // VeRA shrink block: 32 VeRA rows x 32 ranks of A_sh over one K slice
+      // of 256 (one round of loads), scaled by d (per rank, so it commutes
+      // with the K sum) and added into the row's VeRA slots. The block
+      // follows from the item index, so its row records load at once.
+      const int32_t per_kv = a.nvb * a.njb;
+      const int32_t kv = it / per_kv, vb = (it - kv * per_kv) / a.njb;
+      const int32_t jb = it - kv * per_kv - vb * a.njb;
+      const int m = lane & 31, h = lane >> 5;
+      const DecVeraRow vr = a.vrows[32 * vb + m];
+      const uint16_t* xr = a.x + (size_t)vr.tok * d_in + (int64_t)kv * 256 + 32 * h;
+      const uint16_t* ar = a.A_sh + (size_t)(32 * jb + m) * d_in + (int64_t)kv * 256 + 32 * h;
+      // output element i: VeRA row 32 vb + 8 (i / 4) + 4 h + i % 4, rank 32 jb + m
+      const int32_t j = 32 * jb + m;
+      float dsc[16];
+      int32_t prow[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const DecVeraRow o = a.vrows[32 * vb + 8 * (i >> 2) + 4 * h + (i & 3)];
+        prow[i] = o.p;
+        dsc[i] = ldg(o.vd + j);
+      }
+      const f32x16 acc = shrink_tile(xr, ar);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + a.RT + j, acc[i] * dsc[i]);
+      continue;
+    }
     const DecProItem item = a.items[it];
     if (item.type == PRO_GATHER) {
       // one x row (d_in <= 8192: at most 16 16-byte pieces per lane)
@@ -173,29 +201,6 @@ k_decode_prologue(ProArgs a) {
       const int r = lane >> 2, j = lane & 3;
       if (lane < 16 && r < len && j < nk)
         atomicAdd(a.acc + (size_t)(item.p0 + r) * a.AW + k0 + j, mine);
-    } else if (item.type == PRO_VSHRINK) {
-      // VeRA shrink block: 32 VeRA rows x 32 ranks of A_sh over one K slice
-      // of 256 (one round of loads), scaled by d (per rank, so it commutes
-      // with the K sum) and added into the row's VeRA slots
-      const int32_t vb = item.p0, jb = item.n, kv = item.k;
-      const int m = lane & 31, h = lane >> 5;
-      const DecVeraRow vr = a.vrows[32 * vb + m];
-      const uint16_t* xr = a.x + (size_t)vr.tok * d_in + (int64_t)kv * 256 + 32 * h;
-      const uint16_t* ar = a.A_sh + (size_t)(32 * jb + m) * d_in + (int64_t)kv * 256 + 32 * h;
-      // output element i: VeRA row 32 vb + 8 (i / 4) + 4 h + i % 4, rank 32 jb + m
-      const int32_t j = 32 * jb + m;
-      float dsc[16];
-      int32_t prow[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const DecVeraRow o = a.vrows[32 * vb + 8 * (i >> 2) + 4 * h + (i & 3)];
-        prow[i] = o.p;
-        dsc[i] = ldg(o.vd + j);
-      }
-      const f32x16 acc = shrink_tile(xr, ar);
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + a.RT + j, acc[i] * dsc[i]);
     }
   }
 }
@@ -762,6 +767,9 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
     pa.x = (const uint16_t*)x;
     pa.items = D.pro_items;
     pa.n_items = D.n_pro;
+    pa.n_vitems = D.n_vitems;
+    pa.nvb = D.nvb;
+    pa.njb = D.njb;
     pa.vrows = D.vrows;
     pa.A_sh = (const uint16_t*)L->A_sh;
     pa.xs = D.xs;

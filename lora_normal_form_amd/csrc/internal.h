@@ -140,6 +140,9 @@ struct DecodePlan {
   int32_t C = 0;        // column tiles of 64 outputs
   int32_t k_chunk = 0;  // d_in / S
   int32_t n_pro = 0;    // prologue work items
+  // the first n_vitems prologue items are the VeRA shrinks, item
+  // (kv nvb + vb) njb + jb covering K slice kv, VeRA rows 32 vb.., ranks 32 jb..
+  int32_t n_vitems = 0, nvb = 0, njb = 0;
   int32_t n_steps = 0;
   // [2 S + 1]: the expand steps of slice k's K half h are [2k + h, 2k + h + 1)
   int32_t step_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -293,6 +296,7 @@ struct ProArgs {
   const uint16_t* x;
   const DecProItem* items;
   int32_t n_items;
+  int32_t n_vitems, nvb, njb;  // VeRA shrink items first, indexed arithmetically
   const DecVeraRow* vrows;  // [32 nvb]
   const uint16_t* A_sh;     // [r_v][d_in]
   uint16_t* xs;             // [M_pad + 32 g_rot][d_in] sorted x rows, then delta rows

@@ -335,7 +335,17 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     return rank(p.type) < rank(q.type);
   });
   D.n_pro = (int32_t)pro.size();
-  if (D.n_pro != n_pro) {
+  D.n_vitems = SV * nvb * njb;
+  D.nvb = nvb;
+  D.njb = njb;
+  // the kernel derives a VeRA item's (kv, vb, jb) from its index
+  bool order_ok = D.n_pro == n_pro;
+  for (int32_t i = 0; order_ok && i < D.n_vitems; ++i) {
+    const DecProItem& it = pro[i];
+    order_ok = it.type == PRO_VSHRINK && it.k == i / (nvb * njb) && it.p0 == (i / njb) % nvb &&
+               it.n == i % njb;
+  }
+  if (!order_ok) {
     (void)hipFree(B->fast_dev);
     B->fast_dev = nullptr;
     D = DecodePlan{};
