@@ -309,27 +309,34 @@ __device__ __forceinline__ void kstep(int t, int nst, const WSrc& wrow,
 // stream from HBM, so it runs further ahead than the LDS rows), stages past
 // the last are not prefetched, and the wait counts exactly the loads issued
 // after stage T's rows (R = 3: the next stage's rows and W issued by the
-// previous step; this step's W). Expands to the steps T .. NST-1.
-template <int MGT, int NST, int LW, int T>
+// previous step; this step's W). Expands to the steps T .. NST-1. Step 1
+// also runs `early` after its barrier (NE loads, counted at step 2).
+template <int MGT, int NST, int LW, int T, int NE, typename Early>
 __device__ __forceinline__ void ksteps_static(const WSrc& wrow, const uint16_t* const (&src)[2 * MGT],
                                               uint8_t* s0, uint8_t* s1, uint8_t* s2,
                                               uint4 (&wb)[LW + 1][4], f32x16 (&acc)[MGT], int m,
-                                              int h, int cb, int kp) {
+                                              int h, int cb, int kp, Early& early) {
   if constexpr (T < NST) {
     using Cfg = DecCfg<MGT>;
     constexpr int R = Cfg::R;
     constexpr int TN = T + R - 1;   // rows this step prefetches
     constexpr int TW = T + LW;      // W this step prefetches
     constexpr int allowed = (R == 3 && T + 1 < NST ? 2 * MGT : 0) +
-                            (R == 3 && T - 1 + LW < NST ? 4 : 0) + (TW < NST ? 4 : 0);
+                            (R == 3 && T - 1 + LW < NST ? 4 : 0) + (TW < NST ? 4 : 0) +
+                            (R == 3 && T == 2 ? NE : 0);
     uint8_t* cur = T % R == 0 ? s0 : (T % R == 1 ? s1 : s2);
     uint8_t* nxt = TN % R == 0 ? s0 : (TN % R == 1 ? s1 : s2);
     if constexpr (TW < NST) load_w(wb[TW % (LW + 1)], wrow, (int64_t)SK * TW);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(allowed));
     wg_barrier();
+    if constexpr (T == 1) {
+      issue_fence();
+      early();
+      issue_fence();
+    }
     if constexpr (TN < NST) stage_rows<MGT>(nxt + kp * Cfg::STAGE, src, (int64_t)SK * TN, cb);
     mma_stage<MGT>(cur + kp * Cfg::STAGE, wb[T % (LW + 1)], acc, m, h);
-    ksteps_static<MGT, NST, LW, T + 1>(wrow, src, s0, s1, s2, wb, acc, m, h, cb, kp);
+    ksteps_static<MGT, NST, LW, T + 1, NE>(wrow, src, s0, s1, s2, wb, acc, m, h, cb, kp, early);
   }
 }
 
@@ -507,6 +514,22 @@ k_decode_main(MainArgs a) {
 #pragma unroll
   for (int g = 0; g < MGT; ++g) acc[g] = f32x16{};
 
+  // epilogue layout: 16 threads per row, a float4 of the tile's 64 columns
+  // each; every row's s vector loads during the K loop (step 1, once the row
+  // records are in LDS), so the first row pass does not wait for it
+  const int q4 = tid & 15, rr = tid >> 4;  // float4 of the row, row within 16
+  const int nj = 2 * mgx;                  // passes of 16 rows over the x rows
+  const int64_t cbase = (int64_t)c * 64 + 4 * q4;
+  f32x4 s4[2 * MGT];
+  auto issue_s = [&]() {
+#pragma unroll
+    for (int j = 0; j < 2 * MGT; ++j) {
+      const int r = rr + 16 * min(j, nj - 1);
+      s4[j] = ldg4(rec_ptr(rec[r][0], 0) + cbase);
+    }
+  };
+  constexpr bool s_early = NST >= 2;
+
   // stage 0 (peeled: the row records go to LDS after its barrier)
   {
     constexpr bool pre = NST == 0 || R - 1 < NST;   // rows of stage R-1
@@ -528,7 +551,8 @@ k_decode_main(MainArgs a) {
   // remaining stages; stage t lives in ring slot t % R and W registers
   // wb[t % R], named statically in both forms of the loop
   if constexpr (NST > 0) {
-    ksteps_static<MGT, NST, LW, 1>(wrow, src, slot0, slot1, slot2, wb, acc, m, h, cb, kp);
+    ksteps_static<MGT, NST, LW, 1, s_early ? 2 * MGT : 0>(wrow, src, slot0, slot1, slot2, wb, acc, m,
+                                                        h, cb, kp, issue_s);
   } else if constexpr (R == 3) {
 #pragma unroll 1
     for (int t = 1; t < nst; t += 3) {
@@ -552,18 +576,15 @@ k_decode_main(MainArgs a) {
   // ---- epilogue ---------------------------------------------------------------
   // the first expand batch's operands and the rows' factor vectors are in
   // flight while the K halves meet
+  if constexpr (!s_early) issue_s();
   RawBatch rb;
   if (i0 < i1) issue_batch(a, win, i0, min(NSL, i1 - i0), rb, ncol, m, h);
-  const int q4 = tid & 15, rr = tid >> 4;  // float4 of the row, row within 16
-  const int nj = 2 * mgx;                  // passes of 16 rows over the x rows
-  const int64_t cbase = (int64_t)c * 64 + 4 * q4;
   constexpr bool early_f = MGT <= 6;       // register room to fetch e and b here too
-  f32x4 s4[2 * MGT], e4[2 * MGT], b4[2 * MGT];
+  f32x4 e4[2 * MGT], b4[2 * MGT];
+  if constexpr (early_f) {
 #pragma unroll
-  for (int j = 0; j < 2 * MGT; ++j) {
-    const int r = rr + 16 * min(j, nj - 1);
-    s4[j] = ldg4(rec_ptr(rec[r][0], 0) + cbase);
-    if constexpr (early_f) {
+    for (int j = 0; j < 2 * MGT; ++j) {
+      const int r = rr + 16 * min(j, nj - 1);
       e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
       b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
     }
