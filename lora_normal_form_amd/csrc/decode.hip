@@ -215,6 +215,7 @@ struct MainArgs {
   const DecRow* rows;               // [M_pad]
   const DecStep* steps;             // expand steps by slice and K half
   const float* acc;                 // [M_pad][AW] shrink sums: RT own ranks, then r_v VeRA ranks
+  const uint16_t* B_sh;             // [d_out][r_v] (dense VeRA expand)
   const float* zeros;               // [d_out]
   float* part;                      // [S][C][M_pad][64] split-K partial tiles (S > 1)
   int32_t* cnt;                     // [C] arrival counters, kept at zero between forwards
@@ -222,6 +223,7 @@ struct MainArgs {
   uint32_t acc_bytes, part_bytes;
   int32_t off[9];                   // [2 S + 1]: slice k, K half h: steps [2k + h, 2k + h + 1)
   int32_t g_rot, d_in, d_out, k_chunk, S, C, RT, AW;
+  int32_t gv0, gv1, r_v;            // dense VeRA expand over row groups [gv0, gv1) (gv1 > gv0)
 };
 
 // Tile of the main kernel: 64 output columns (two 32-column MFMA blocks) by
@@ -422,6 +424,96 @@ __device__ __forceinline__ void convert_batch(const StepWin& w, int s0, int nb, 
                                   pack_bf2(a1.x, a1.y), pack_bf2(a1.z, a1.w));
       ob.b[j] = ok ? rb.b[j] : make_uint4(0, 0, 0, 0);
       ob.a[j] = (ok && rowok) ? av : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// Dense VeRA expand of one slice: the VeRA rows' products u B_sh over the
+// slice's share [16 ks0, 16 ks1) of the r_v ranks, for row groups
+// [gv0, gv1) (rows there without a VeRA term have zero sums). In chunks of up
+// to 128 ranks, the work-group stages the rows' sums as bf16 in V's LDS
+// buffer (rows of 16 pieces of 16 bytes, piece p of row r at p ^ (r & 15), so
+// the MFMA reads of 16 rows hit 16 different bank groups) and each wave
+// multiplies its groups (K half kp takes every other group) in registers,
+// with its column's B_sh pieces for every rank step loaded once up front.
+// The products go to V after every wave is done reading the staged sums.
+template <int MGT>
+__device__ __forceinline__ void dense_vera(const MainArgs& a, float* V, int32_t* vflag, int kc,
+                                           int cb, int kp, int tid, int m, int h, int64_t ncol) {
+  constexpr int MAXG = (MGT + 1) / 2;  // groups per wave
+  const int nks = a.r_v / 16;
+  const int ks0 = kc * nks / a.S, ks1 = (kc + 1) * nks / a.S, nk = ks1 - ks0;
+  if (nk <= 0) return;  // uniform over the work-group
+  const int rows = 32 * (a.gv1 - a.gv0);
+  uint8_t* U = reinterpret_cast<uint8_t*>(V);
+  // this lane's B_sh pieces: rank 16 (ks0 + ks) + 8 h .. + 7 of column ncol
+  uint4 b[16];
+  {
+    const rsrc_t br = make_rsrc(a.B_sh, (uint32_t)((size_t)a.d_out * a.r_v * 2));
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      if (ks < nk) b[ks] = ldb16(br, (uint32_t)((ncol * a.r_v + 16 * (ks0 + ks) + 8 * h) * 2));
+  }
+  const rsrc_t ar = make_rsrc(a.acc, a.acc_bytes);
+  f32x16 vacc[MAXG];
+#pragma unroll
+  for (int q = 0; q < MAXG; ++q) vacc[q] = f32x16{};
+#pragma unroll
+  for (int ch = 0; ch < 2; ++ch) {
+    const int k0 = 8 * ch, kn = min(8, nk - k0);
+    if (kn <= 0) break;  // uniform
+    if (ch > 0) lds_barrier();  // every wave is done with the previous chunk
+    // stage piece p (8 ranks) of row r: 2 kn pieces per row, at most 16 per thread
+    const int pr = 2 * kn, pieces = rows * pr;
+    u32x4 raw[16][2];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int pi = tid + 256 * q;
+      if (pi < pieces) {
+        const int r = pi / pr, p = pi - r * pr;
+        const uint32_t off = (uint32_t)((((int64_t)(32 * a.gv0 + r) * a.AW) + a.RT +
+                                         16 * (ks0 + k0) + 8 * p) * 4);
+        raw[q][0] = __builtin_bit_cast(u32x4, ldb16(ar, off));
+        raw[q][1] = __builtin_bit_cast(u32x4, ldb16(ar, off + 16));
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int pi = tid + 256 * q;
+      if (pi < pieces) {
+        const int r = pi / pr, p = pi - r * pr;
+        const u32x4 v0 = raw[q][0], v1 = raw[q][1];
+        const u32x4 o = u32x4{pack_bf2(v0.x, v0.y), pack_bf2(v0.z, v0.w), pack_bf2(v1.x, v1.y),
+                              pack_bf2(v1.z, v1.w)};
+        *reinterpret_cast<u32x4*>(U + (16 * r + (p ^ (r & 15))) * 16) = o;
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < MAXG; ++q) {
+      const int g = a.gv0 + kp + 2 * q;
+      if (g < a.gv1) {
+        const int r = 32 * (g - a.gv0) + m;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          if (ks < kn) {
+            const uint4 av =
+                *reinterpret_cast<const uint4*>(U + (16 * r + ((2 * ks + h) ^ (r & 15))) * 16);
+            vacc[q] = mfma32(av, b[k0 + ks], vacc[q]);
+          }
+        }
+      }
+    }
+  }
+  lds_barrier();  // every wave is done with the staged sums
+#pragma unroll
+  for (int q = 0; q < MAXG; ++q) {
+    const int g = a.gv0 + kp + 2 * q;
+    if (g < a.gv1) {
+      float* Vg = V + 32 * g * 64 + cb * 32 + m;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Vg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] = vacc[q][i];
+      if (tid == 0 || tid == 64 || tid == 128 || tid == 192) vflag[g] = 1;
     }
   }
 }
@@ -688,6 +780,7 @@ k_decode_main(MainArgs a) {
       if (lane == 0) vflag[cg] = 1;
     }
   }
+  if (a.gv1 > a.gv0) dense_vera<MGT>(a, V, vflag, kc, cb, kp, tid, m, h, ncol);
   wg_barrier();
 
   // (d) row pass 2: this slice's tile = T + (V (.) e) + b (b on slice 0 only)
@@ -829,6 +922,10 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.C = D.C;
   ma.RT = D.RT;
   ma.AW = D.AW;
+  ma.B_sh = (const uint16_t*)L->B_sh;
+  ma.gv0 = D.gv0;
+  ma.gv1 = D.gv1;
+  ma.r_v = L->r_v;
   const dim3 grid(D.C, D.S);
   ProfScope ps(L, st, "decode_main");
   switch (D.MG + D.g_rot) {

@@ -144,6 +144,10 @@ struct DecodePlan {
   // (kv nvb + vb) njb + jb covering K slice kv, VeRA rows 32 vb.., ranks 32 jb..
   int32_t n_vitems = 0, nvb = 0, njb = 0;
   int32_t n_steps = 0;
+  // dense VeRA expand: row groups [gv0, gv1) hold every VeRA row; slice k
+  // multiplies their shrink sums over its share of the r_v / 16 rank steps
+  // (staged in LDS) instead of VeRA steps (gv1 == gv0: no dense expand)
+  int32_t gv0 = 0, gv1 = 0;
   // [2 S + 1]: the expand steps of slice k's K half h are [2k + h, 2k + h + 1)
   int32_t step_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
   const DecRow* rows = nullptr;          // [M_pad]

@@ -123,7 +123,30 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
                              (const uint16_t*)E.B});
     }
   }
+  // The VeRA term can run dense when a slice has at most 256 ranks of it and
+  // the VeRA rows' groups fit the LDS buffer the kernel stages them in, 128
+  // ranks at a time (32 (gv1 - gv0) rows of 256 bytes, at most 256 rows).
   if (B->n_vera > 0) {
+    int32_t pmin = n, pmax = -1;
+    for (int32_t v : B->vera_pos) {
+      pmin = std::min(pmin, v);
+      pmax = std::max(pmax, v);
+    }
+    const int32_t gv0 = pmin / 32, gv1 = pmax / 32 + 1;
+    const int32_t nks = L->r_v / 16, nkmax = (nks + S - 1) / S;
+    const int32_t rows = 32 * (gv1 - gv0);
+    const int64_t slot_bytes = (int64_t)8192 * (D.MG + D.g_rot);
+    // worth it once a slice has 16 or more VeRA rank steps (otherwise the
+    // steps take about one batch); SCUTE_DECODE_DENSE_VERA=1 / 0 forces it
+    // on (where it fits) / off
+    const int32_t mode = env_int("SCUTE_DECODE_DENSE_VERA", -1);
+    const bool fits = nkmax <= 16 && rows <= 256 && (int64_t)rows * 256 <= slot_bytes;
+    if (fits && (mode == 1 || (mode == -1 && (gv1 - gv0) * nkmax >= 16))) {
+      D.gv0 = gv0;
+      D.gv1 = gv1;
+    }
+  }
+  if (B->n_vera > 0 && D.gv1 == D.gv0) {
     for (int32_t g = 0; g < D.MG; ++g) {
       bool any = false;
       for (int32_t p = 32 * g; p < std::min(n, 32 * g + 32); ++p) any |= row_vera[p] != 0;

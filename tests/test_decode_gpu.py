@@ -166,3 +166,21 @@ def test_decode_repeated_forwards_reuse_counters():
         ld.layer.forward(ld.batch, ld.x, ld.W, ld.y)
         torch.cuda.synchronize()
         _check(wl, ld.y.cpu().numpy().astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("shape", [(200, 512, 384, 64), (256, 512, 14336, 256)])
+def test_decode_dense_vera_matches_steps(shape):
+    # the VeRA term as a dense product over LDS-staged sums (one split of the
+    # ranks per K slice; one slice over all 256 ranks for the wide layer)
+    # against the same term as expand steps
+    _need_gpu()
+    n, d_in, d_out, r_v = shape
+    ads = [AdapterSpec("vera"), AdapterSpec("ia3"), AdapterSpec("vera", bias=True),
+           AdapterSpec("lora", rank=16)]
+    wl = _wl(n, seed=41, d_in=d_in, d_out=d_out, vera_rank=r_v, none_frac=0.05, adapters=ads)
+    ref = oracle.forward(wl)
+    _, yd = _forward(wl, expect_path=1, SCUTE_DECODE_DENSE_VERA=1)
+    _check(wl, yd, ref)
+    _, ys = _forward(wl, expect_path=1, SCUTE_DECODE_DENSE_VERA=0)
+    _check(wl, ys, ref)
+    assert np.max(np.abs(yd - ys)) <= 1e-3 * np.max(np.abs(ref))
