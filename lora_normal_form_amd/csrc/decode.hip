@@ -721,13 +721,27 @@ k_decode_main(MainArgs a) {
   wg_barrier();
 
   // (c) expand: batches of NSL steps, the next batch's operands loading
-  //     while this one multiplies. Own steps sum one item's product in
-  //     registers and add it into T on the rows of its segment; VeRA steps
-  //     of one row group sum into one fragment that goes to V. The two K-half
-  //     waves of a column block hold disjoint segments and groups.
+  //     while this one multiplies. Own steps of one row group sum in
+  //     registers (their A rows are zero outside each item's segment) and
+  //     are added into T on the rows of this wave's segments (a row mask),
+  //     reading all 16 values before writing any; VeRA steps of one row group
+  //     sum into one fragment that goes to V. The two K-half waves of a
+  //     column block hold disjoint segments and groups.
   {
-    int cg = -1;
+    int cg = -1, og = -1;
+    uint32_t omask = 0u;  // rows of group og that this wave's own items cover
     f32x16 t2 = {}, vacc = {};
+    auto flush_own = [&]() {
+      float* Tg = T + 32 * og * 64 + cb * 32 + m;
+      float old[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) old[i] = Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
+        if ((omask >> r) & 1u) Tg[r * 64] = old[i] + t2[i];
+      }
+    };
     for (int sc = i0; sc < i1;) {
       const int nb = min(NSL, i1 - sc);
       OpBatch ob;
@@ -755,16 +769,14 @@ k_decode_main(MainArgs a) {
           }
           vacc = mfma32(ob.a[j], ob.b[j], vacc);
         } else {
-          t2 = mfma32(ob.a[j], ob.b[j], t2);
-          if (d.gk & STEP_LAST) {
-            float* Tg = T + 32 * gi * 64 + cb * 32 + m;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-              if (32 * gi + r >= d.lo && 32 * gi + r < d.hi) Tg[r * 64] += t2[i];
-            }
+          if (gi != og) {
+            if (og >= 0) flush_own();
+            og = gi;
+            omask = 0u;
             t2 = f32x16{};
           }
+          t2 = mfma32(ob.a[j], ob.b[j], t2);
+          omask |= (uint32_t)((((uint64_t)1 << (d.hi - d.lo)) - 1) << (d.lo - 32 * gi));
         }
       }
       if (sn < i1 && !same_win) {
@@ -773,6 +785,7 @@ k_decode_main(MainArgs a) {
       }
       sc = sn;
     }
+    if (og >= 0) flush_own();
     if (cg >= 0) {
       float* Vg = V + 32 * cg * 64 + cb * 32 + m;
 #pragma unroll
