@@ -213,7 +213,8 @@ struct MainArgs {
   const uint16_t* xs;               // [32 MGT][d_in] sorted x rows, then delta rows
   const uint16_t* W;
   const DecRow* rows;               // [M_pad]
-  const DecStep* steps;             // expand steps by slice and K half
+  const DecStep* steps;             // expand steps by slice and row group
+  const int32_t* goff;              // [2 S MG + 1] step ranges, below
   const float* acc;                 // [M_pad][AW] shrink sums: RT own ranks, then r_v VeRA ranks
   const uint16_t* B_sh;             // [d_out][r_v] (dense VeRA expand)
   const float* zeros;               // [d_out]
@@ -221,7 +222,9 @@ struct MainArgs {
   int32_t* cnt;                     // [C] arrival counters, kept at zero between forwards
   float* y;
   uint32_t acc_bytes, part_bytes;
-  int32_t off[9];                   // [2 S + 1]: slice k, K half h: steps [2k + h, 2k + h + 1)
+  // slice k, row group g (q = k MG + g): own steps [goff[2q], goff[2q+1]),
+  // VeRA steps [goff[2q+1], goff[2q+2])
+  int32_t MG;
   int32_t g_rot, d_in, d_out, k_chunk, S, C, RT, AW;
   int32_t gv0, gv1, r_v;            // dense VeRA expand over row groups [gv0, gv1) (gv1 > gv0)
 };
@@ -380,50 +383,75 @@ __device__ __forceinline__ StepDesc step_at(const StepWin& w, int j) {
   return d;
 }
 
-// A batch of up to NSL steps: raw operands as loaded (A: the row's 8 fp32
-// shrink sums of the lane's k half; B: 8 bf16 of the lane's column of B' or
-// B_sh), then the MFMA operands (A rounded to bf16; rows outside the step's
-// [lo, hi) and ranks past the term's rank zeroed). Loads go through buffer
-// resources, so nothing past an operand is read.
-constexpr int NSL = 8;
-struct RawBatch {
-  uint4 b[NSL], a0[NSL], a1[NSL];
+// Operands of one 16-rank expand step for lane (m, h) and both 32-column
+// blocks of the tile: A = row 32 g + m's 8 shrink sums of ranks kk + 8 h ..
+// (fp32 as stored), B = 8 bf16 of B' (or B_sh) row ncol (+ 32) from rank
+// kk + 8 h. Loads go through buffer resources, so nothing past an operand
+// is read (ranks past the term's rank read zeros or are zeroed below).
+struct StepOps {
+  uint4 a0, a1, b0, b1;
+  int32_t ok;  // lane's row inside the step's rows and ranks inside the term
 };
-struct OpBatch {
-  uint4 a[NSL], b[NSL];
-};
-__device__ __forceinline__ void issue_batch(const MainArgs& a, const StepWin& w, int s0, int nb,
-                                            RawBatch& rb, int64_t ncol, int m, int h) {
+__device__ __forceinline__ StepOps load_step(const MainArgs& a, const StepDesc& d, int g,
+                                             int64_t ncol, int m, int h) {
+  StepOps o;
+  const int kk = d.kk + 8 * h;
+  const int row = 32 * g + m;
+  const int acol = (d.gk & STEP_VERA) ? a.RT : 0;
   const rsrc_t ar = make_rsrc(a.acc, a.acc_bytes);
-#pragma unroll
-  for (int j = 0; j < NSL; ++j) {
-    if (j < nb) {
-      const StepDesc d = step_at(w, s0 - w.base + j);
-      const int gi = d.gk >> 8;
-      const int kk = d.kk + 8 * h;  // the lane's first rank
-      const int acol = (d.gk & STEP_VERA) ? a.RT : 0;
-      const rsrc_t br = make_rsrc(d.bp, (uint32_t)(a.d_out * d.rank * 2));
-      rb.b[j] = ldb16(br, (uint32_t)((ncol * d.rank + kk) * 2));
-      const uint32_t ao = (uint32_t)(((int64_t)(32 * gi + m) * a.AW + acol + kk) * 4);
-      rb.a0[j] = ldb16(ar, ao);
-      rb.a1[j] = ldb16(ar, ao + 16);
-    }
-  }
+  const rsrc_t br = make_rsrc(d.bp, (uint32_t)(a.d_out * d.rank * 2));
+  const uint32_t ao = (uint32_t)(((int64_t)row * a.AW + acol + kk) * 4);
+  o.a0 = ldb16(ar, ao);
+  o.a1 = ldb16(ar, ao + 16);
+  o.b0 = ldb16(br, (uint32_t)((ncol * d.rank + kk) * 2));
+  o.b1 = ldb16(br, (uint32_t)(((ncol + 32) * d.rank + kk) * 2));
+  o.ok = kk < d.rank && row >= d.lo && row < d.hi;
+  return o;
 }
-__device__ __forceinline__ void convert_batch(const StepWin& w, int s0, int nb, const RawBatch& rb,
-                                              OpBatch& ob, int m, int h) {
+__device__ __forceinline__ void mma_step(const StepOps& o, f32x16& c0, f32x16& c1) {
+  const uint4 av = o.ok ? make_uint4(pack_bf2(o.a0.x, o.a0.y), pack_bf2(o.a0.z, o.a0.w),
+                                     pack_bf2(o.a1.x, o.a1.y), pack_bf2(o.a1.z, o.a1.w))
+                        : make_uint4(0, 0, 0, 0);
+  c0 = mfma32(av, o.b0, c0);
+  c1 = mfma32(av, o.b1, c1);
+}
+// Up to NB steps' operands, loaded together (one memory round trip per
+// batch); the window must hold the descriptors of steps [s, s + NB) that
+// exist (those below e1).
+template <int NB>
+struct StepBatch {
+  StepOps o[NB];
+};
+template <int NB>
+__device__ __forceinline__ void load_batch(const MainArgs& a, const StepWin& w, int s, int e1,
+                                           int g, int64_t ncol, int m, int h, StepBatch<NB>& b) {
 #pragma unroll
-  for (int j = 0; j < NSL; ++j) {
-    if (j < nb) {
-      const StepDesc d = step_at(w, s0 - w.base + j);
-      const int pa = 32 * (d.gk >> 8) + m;
-      const bool ok = d.kk + 8 * h < d.rank;
-      const bool rowok = pa >= d.lo && pa < d.hi;
-      const uint4 a0 = rb.a0[j], a1 = rb.a1[j];
-      const uint4 av = make_uint4(pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w),
-                                  pack_bf2(a1.x, a1.y), pack_bf2(a1.z, a1.w));
-      ob.b[j] = ok ? rb.b[j] : make_uint4(0, 0, 0, 0);
-      ob.a[j] = (ok && rowok) ? av : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < NB; ++j)
+    if (s + j < e1) b.o[j] = load_step(a, step_at(w, s + j - w.base), g, ncol, m, h);
+}
+// The expand of one row group in this slice: steps [e0, ev) are own steps
+// (summed into o0 / o1), [ev, e1) VeRA steps (into v0 / v1), for column
+// blocks 0 / 1. `b` holds the first batch already when `loaded`; the window
+// `w` starts at e0.
+template <int NB>
+__device__ __forceinline__ void expand_group(const MainArgs& a, StepWin& w, StepBatch<NB>& b,
+                                             bool loaded, int e0, int ev, int e1, int g,
+                                             int64_t ncol, int m, int h, int lane, f32x16& o0,
+                                             f32x16& o1, f32x16& v0, f32x16& v1) {
+  for (int s = e0; s < e1; s += NB) {
+    if (s != e0 || !loaded) {
+      if (s + NB > w.base + 64 && e1 > w.base + 64) load_win(a.steps, w, s, e1, lane);
+      load_batch(a, w, s, e1, g, ncol, m, h, b);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int st = s + j;
+      if (st < e1) {
+        if (st < ev)
+          mma_step(b.o[j], o0, o1);
+        else
+          mma_step(b.o[j], v0, v1);
+      }
     }
   }
 }
@@ -591,16 +619,17 @@ k_decode_main(MainArgs a) {
   }
   stage_rows<MGT>(slot0 + kp * Cfg::STAGE, src, 0, cb);
   if constexpr (pre1) stage_rows<MGT>(slot1 + kp * Cfg::STAGE, src, (int64_t)SK * min(1, nst - 1), cb);
-  // (3) this wave's expand steps (its K half's share of the slice's items);
-  //     the first 64 descriptors load now and are used after the K loop
-  int i0 = 0, i1 = 0;
-#pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    if (i == 2 * kc + kp) i0 = a.off[i];
-    if (i == 2 * kc + kp + 1) i1 = a.off[i];
+  // (3) the expand steps of this wave's first row group (row group `wave`
+  //     of the x rows): its step range and first 64 descriptors load now
+  int g_e0 = 0, g_ev = 0, g_e1 = 0;
+  if (wave < mgx) {
+    const int q = 2 * (kc * a.MG + wave);
+    g_e0 = uni(a.goff[q]);
+    g_ev = uni(a.goff[q + 1]);
+    g_e1 = uni(a.goff[q + 2]);
   }
   StepWin win;
-  load_win(a.steps, win, i0, i1, lane);
+  load_win(a.steps, win, g_e0, g_e1, lane);
 
   f32x16 acc[MGT];
 #pragma unroll
@@ -668,9 +697,11 @@ k_decode_main(MainArgs a) {
   // ---- epilogue ---------------------------------------------------------------
   // the first expand batch's operands and the rows' factor vectors are in
   // flight while the K halves meet
+  const int64_t ncol0 = (int64_t)c * 64 + m;
+  constexpr int NB = MGT <= 5 ? 8 : 4;  // register room
+  StepBatch<NB> sb;
+  load_batch(a, win, g_e0, g_e1, wave, ncol0, m, h, sb);
   if constexpr (!s_early) issue_s();
-  RawBatch rb;
-  if (i0 < i1) issue_batch(a, win, i0, min(NSL, i1 - i0), rb, ncol, m, h);
   constexpr bool early_f = MGT <= 6;       // register room to fetch e and b here too
   f32x4 e4[2 * MGT], b4[2 * MGT];
   if constexpr (early_f) {
@@ -686,20 +717,13 @@ k_decode_main(MainArgs a) {
   //     of group g is row 32 g + 8 (i / 4) + 4 h + i % 4, column cb 32 + m
   float* T = reinterpret_cast<float*>(slot0);
   float* V = reinterpret_cast<float*>(slot1);
-  if (kp == 1) {
+  {
+    float* Tk = kp == 0 ? V : T;  // K half 0 -> V, K half 1 -> T
 #pragma unroll
     for (int g = 0; g < MGT; ++g)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        T[(32 * g + 8 * (i >> 2) + 4 * h + (i & 3)) * 64 + cb * 32 + m] = acc[g][i];
-  }
-  wg_barrier();
-  if (kp == 0) {
-#pragma unroll
-    for (int g = 0; g < MGT; ++g)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        T[(32 * g + 8 * (i >> 2) + 4 * h + (i & 3)) * 64 + cb * 32 + m] += acc[g][i];
+        Tk[(32 * g + 8 * (i >> 2) + 4 * h + (i & 3)) * 64 + cb * 32 + m] = acc[g][i];
   }
   wg_barrier();
 
@@ -708,89 +732,59 @@ k_decode_main(MainArgs a) {
   f32x4* T4 = reinterpret_cast<f32x4*>(T);
   f32x4* V4 = reinterpret_cast<f32x4*>(V);
   {
+    f32x4 v[2 * MGT], dv[2 * MGT];
 #pragma unroll
     for (int j = 0; j < 2 * MGT; ++j) {
-      if (j < nj) {
-        const int r = rr + 16 * j;
-        f32x4 v = T4[r * 16 + q4];
-        if (j < 2 * a.g_rot) v += T4[(Mx + r) * 16 + q4];
-        T4[r * 16 + q4] = v * s4[j];
-      }
+      const int r = rr + 16 * min(j, nj - 1);
+      v[j] = T4[r * 16 + q4] + V4[r * 16 + q4];
+      dv[j] = j < 2 * a.g_rot ? T4[(Mx + r) * 16 + q4] + V4[(Mx + r) * 16 + q4]
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int j = 0; j < 2 * MGT; ++j)
+      if (j < nj) T4[(rr + 16 * j) * 16 + q4] = (v[j] + dv[j]) * s4[j];
   }
   wg_barrier();
 
-  // (c) expand: batches of NSL steps, the next batch's operands loading
-  //     while this one multiplies. Own steps of one row group sum in
-  //     registers (their A rows are zero outside each item's segment) and
-  //     are added into T on the rows of this wave's segments (a row mask),
-  //     reading all 16 values before writing any; VeRA steps of one row group
-  //     sum into one fragment that goes to V. The two K-half waves of a
-  //     column block hold disjoint segments and groups.
-  {
-    int cg = -1, og = -1;
-    uint32_t omask = 0u;  // rows of group og that this wave's own items cover
-    f32x16 t2 = {}, vacc = {};
-    auto flush_own = [&]() {
-      float* Tg = T + 32 * og * 64 + cb * 32 + m;
-      float old[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) old[i] = Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64];
+  // (c) expand: wave w takes row groups w, w + 4, .. of the x rows and both
+  //     column blocks. A group's own steps (A rows zero outside each step's
+  //     segment) sum in registers and are added into T's rows of the group
+  //     (every read before any write); its VeRA steps sum into V's rows of
+  //     the group. No two waves touch the same rows.
+  for (int g = wave; g < mgx; g += 4) {
+    int e0 = g_e0, ev = g_ev, e1 = g_e1;
+    if (g != wave) {
+      const int q = 2 * (kc * a.MG + g);
+      e0 = uni(a.goff[q]);
+      ev = uni(a.goff[q + 1]);
+      e1 = uni(a.goff[q + 2]);
+      load_win(a.steps, win, e0, e1, lane);
+    }
+    if (e1 <= e0) continue;
+    f32x16 o0 = {}, o1 = {}, v0 = {}, v1 = {};
+    expand_group(a, win, sb, g == wave, e0, ev, e1, g, ncol0, m, h, lane, o0, o1, v0, v1);
+    if (ev > e0) {
+      float* Tg = T + 32 * g * 64 + m;
+      float old[32];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * h + (i & 3);
-        if ((omask >> r) & 1u) Tg[r * 64] = old[i] + t2[i];
+        old[i] = Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64];
+        old[16 + i] = Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64 + 32];
       }
-    };
-    for (int sc = i0; sc < i1;) {
-      const int nb = min(NSL, i1 - sc);
-      OpBatch ob;
-      convert_batch(win, sc, nb, rb, ob, m, h);
-      const int sn = sc + nb;
-      // the next batch stays in this window (batches start at i0 + NSL t and
-      // a window holds 64 / NSL of them)
-      const bool same_win = sn < i1 && sn + min(NSL, i1 - sn) <= win.base + 64;
-      if (same_win) issue_batch(a, win, sn, min(NSL, i1 - sn), rb, ncol, m, h);
 #pragma unroll
-      for (int j = 0; j < NSL; ++j) {
-        if (j >= nb) continue;
-        const StepDesc d = step_at(win, sc - win.base + j);
-        const int gi = d.gk >> 8;
-        if (d.gk & STEP_VERA) {
-          if (gi != cg) {
-            if (cg >= 0) {
-              float* Vg = V + 32 * cg * 64 + cb * 32 + m;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) Vg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] = vacc[i];
-              if (lane == 0) vflag[cg] = 1;
-            }
-            cg = gi;
-            vacc = f32x16{};
-          }
-          vacc = mfma32(ob.a[j], ob.b[j], vacc);
-        } else {
-          if (gi != og) {
-            if (og >= 0) flush_own();
-            og = gi;
-            omask = 0u;
-            t2 = f32x16{};
-          }
-          t2 = mfma32(ob.a[j], ob.b[j], t2);
-          omask |= (uint32_t)((((uint64_t)1 << (d.hi - d.lo)) - 1) << (d.lo - 32 * gi));
-        }
+      for (int i = 0; i < 16; ++i) {
+        Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] = old[i] + o0[i];
+        Tg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64 + 32] = old[16 + i] + o1[i];
       }
-      if (sn < i1 && !same_win) {
-        load_win(a.steps, win, sn, i1, lane);
-        issue_batch(a, win, sn, min(NSL, i1 - sn), rb, ncol, m, h);
-      }
-      sc = sn;
     }
-    if (og >= 0) flush_own();
-    if (cg >= 0) {
-      float* Vg = V + 32 * cg * 64 + cb * 32 + m;
+    if (e1 > ev) {
+      float* Vg = V + 32 * g * 64 + m;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) Vg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] = vacc[i];
-      if (lane == 0) vflag[cg] = 1;
+      for (int i = 0; i < 16; ++i) {
+        Vg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64] = v0[i];
+        Vg[(8 * (i >> 2) + 4 * h + (i & 3)) * 64 + 32] = v1[i];
+      }
+      if (lane == 0) vflag[g] = 1;
     }
   }
   if (a.gv1 > a.gv0) dense_vera<MGT>(a, V, vflag, kc, cb, kp, tid, m, h, ncol);
@@ -926,7 +920,8 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.y = y;
   ma.acc_bytes = D.acc_bytes;
   ma.part_bytes = D.part_bytes;
-  for (int i = 0; i < 9; ++i) ma.off[i] = D.step_off[i];
+  ma.goff = D.goff;
+  ma.MG = D.MG;
   ma.g_rot = D.g_rot;
   ma.d_in = (int32_t)L->d_in;
   ma.d_out = (int32_t)L->d_out;

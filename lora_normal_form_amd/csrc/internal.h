@@ -104,11 +104,11 @@ enum : int32_t { PRO_ROT = 0, PRO_SHRINK = 1, PRO_VSHRINK = 2, PRO_GATHER = 3 };
 // One 16-rank step of the decode main kernel's expand: an MFMA step over
 // ranks [kk, kk + 16) of one row group's own term (t B' against the
 // adapter's B') or shared VeRA term (u B_sh). 32 bytes.
-//   gk   kind (STEP_VERA) | STEP_LAST on an own item's last step | group << 8
+//   gk   kind (STEP_VERA) | group << 8
 //   kk   first rank of the step; rank = length of a B row (the term's rank)
 //   lohi sorted rows [lo, hi) of the group the step contributes to
 //   bp   B' of the adapter, or B_sh
-enum : int32_t { STEP_VERA = 1, STEP_LAST = 2 };
+enum : int32_t { STEP_VERA = 1 };
 struct DecStep {
   int32_t gk, kk, rank, lohi;
   const uint16_t* bp;
@@ -148,8 +148,9 @@ struct DecodePlan {
   // multiplies their shrink sums over its share of the r_v / 16 rank steps
   // (staged in LDS) instead of VeRA steps (gv1 == gv0: no dense expand)
   int32_t gv0 = 0, gv1 = 0;
-  // [2 S + 1]: the expand steps of slice k's K half h are [2k + h, 2k + h + 1)
-  int32_t step_off[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0};
+  // [2 S MG + 1] step ranges: slice k, row group g (q = k MG + g) has own
+  // steps [goff[2q], goff[2q+1]) and VeRA steps [goff[2q+1], goff[2q+2])
+  const int32_t* goff = nullptr;
   const DecRow* rows = nullptr;          // [M_pad]
   const DecProItem* pro_items = nullptr; // [n_pro]
   const DecVeraRow* vrows = nullptr;     // [32 nvb]

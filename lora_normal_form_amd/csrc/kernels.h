@@ -117,8 +117,13 @@ __device__ __forceinline__ const uint16_t* uni_ptr(const uint16_t* p) {
   return (const uint16_t*)(((uint64_t)(uint32_t)uni((int)(v >> 32)) << 32) |
                            (uint32_t)uni((int)(uint32_t)v));
 }
+// two fp32 values (bit patterns) -> packed bf16, round to nearest even (one
+// v_cvt_pk_bf16_f32 on gfx950)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(uint32_t lo, uint32_t hi) {
-  return (uint32_t)f2bf(__uint_as_float(lo)) | ((uint32_t)f2bf(__uint_as_float(hi)) << 16);
+  const f32x2 v = {__uint_as_float(lo), __uint_as_float(hi)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // One 32x32 shrink tile over a K slice of 256 on 32x32x16 MFMA: lane (m, h)

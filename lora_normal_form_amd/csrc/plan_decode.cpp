@@ -156,83 +156,43 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
                               32 * g + 32, (const uint16_t*)L->B_sh});
     }
   }
-  // spread each kind over the S slices (greedy by steps)
-  auto spread = [&](std::vector<Item>& items) {
+  // Each row group's items spread over the S slices, largest first, each to
+  // the slice with the fewest of the group's steps so far. In the main
+  // kernel one wave runs a group's steps of its slice: the own items' steps,
+  // then the VeRA items' steps.
+  const int32_t MG = D.MG;
+  std::vector<std::vector<Item>> per((size_t)S * MG * 2);  // [(k MG + g) 2 + vera]
+  for (int32_t g = 0; g < MG; ++g) {
+    std::vector<Item> items;
+    for (const Item& it : own_items)
+      if (it.g == g) items.push_back(it);
+    for (const Item& it : vera_items)
+      if (it.g == g) items.push_back(it);
     std::stable_sort(items.begin(), items.end(),
                      [](const Item& p, const Item& q) { return p.nst > q.nst; });
-    std::vector<std::vector<Item>> per(S);
     std::vector<int64_t> load(S, 0);
     for (const Item& it : items) {
-      const int32_t best = (int32_t)(std::min_element(load.begin(), load.end()) - load.begin());
-      per[best].push_back(it);
-      load[best] += it.nst;
-    }
-    return per;
-  };
-  const auto own_per = spread(own_items), vera_per = spread(vera_items);
-  // Within a slice the two K-half waves of a column block share the expand.
-  // A unit (an own term's items of one adapter segment in one group, or a
-  // group's VeRA items) goes to one wave whole, so the two waves write
-  // disjoint rows of the row tile (own) and disjoint groups of the VeRA tile;
-  // units go to the wave with fewer steps so far, largest first. Each wave's
-  // VeRA steps are ordered by group (one group's products sum in registers).
-  std::vector<DecStep> steps;
-  for (int32_t k = 0; k < S; ++k) {
-    std::vector<std::vector<Item>> units;
-    {
-      std::vector<Item> own(own_per[k]);
-      std::stable_sort(own.begin(), own.end(), [](const Item& p, const Item& q) {
-        return p.lo != q.lo ? p.lo < q.lo : p.k < q.k;
-      });
-      for (const Item& it : own) {
-        if (units.empty() || units.back()[0].kind != 0 || units.back()[0].lo != it.lo ||
-            units.back()[0].hi != it.hi || units.back()[0].ptr != it.ptr)
-          units.push_back({});
-        units.back().push_back(it);
-      }
-      std::vector<Item> vera(vera_per[k]);
-      std::stable_sort(vera.begin(), vera.end(), [](const Item& p, const Item& q) {
-        return p.g != q.g ? p.g < q.g : p.k < q.k;
-      });
-      for (const Item& it : vera) {
-        if (units.empty() || units.back()[0].kind != STEP_VERA || units.back()[0].g != it.g)
-          units.push_back({});
-        units.back().push_back(it);
-      }
-    }
-    std::vector<int32_t> ord(units.size());
-    std::vector<int64_t> cost(units.size(), 0);
-    for (size_t u = 0; u < units.size(); ++u) {
-      ord[u] = (int32_t)u;
-      for (const Item& it : units[u]) cost[u] += it.nst;
-    }
-    std::stable_sort(ord.begin(), ord.end(), [&](int32_t p, int32_t q) { return cost[p] > cost[q]; });
-    std::vector<int32_t> half(units.size(), 0);
-    int64_t load[2] = {0, 0};
-    for (int32_t u : ord) {
-      half[u] = load[1] < load[0] ? 1 : 0;
-      load[half[u]] += cost[u];
-    }
-    for (int32_t hh = 0; hh < 2; ++hh) {
-      D.step_off[2 * k + hh] = (int32_t)steps.size();
-      // own units first, then VeRA units in group order (units are built in
-      // that order)
-      for (size_t u = 0; u < units.size(); ++u) {
-        if (half[u] != hh) continue;
-        for (const Item& it : units[u])
-          for (int32_t st = 0; st < it.nst; ++st) {
-            DecStep d{};
-            d.gk = it.kind | (it.kind == 0 && st == it.nst - 1 ? STEP_LAST : 0) | (it.g << 8);
-            d.kk = it.k + 16 * st;
-            d.rank = it.rank;
-            d.lohi = it.lo | (it.hi << 16);
-            d.bp = it.ptr;
-            steps.push_back(d);
-          }
-      }
+      const int32_t k = (int32_t)(std::min_element(load.begin(), load.end()) - load.begin());
+      per[((size_t)k * MG + g) * 2 + (it.kind == STEP_VERA ? 1 : 0)].push_back(it);
+      load[k] += it.nst;
     }
   }
-  D.step_off[2 * S] = (int32_t)steps.size();
+  std::vector<DecStep> steps;
+  std::vector<int32_t> goff;
+  for (size_t q = 0; q < per.size(); ++q) {
+    goff.push_back((int32_t)steps.size());
+    for (const Item& it : per[q])
+      for (int32_t st = 0; st < it.nst; ++st) {
+        DecStep d{};
+        d.gk = it.kind | (it.g << 8);
+        d.kk = it.k + 16 * st;
+        d.rank = it.rank;
+        d.lohi = it.lo | (it.hi << 16);
+        d.bp = it.ptr;
+        steps.push_back(d);
+      }
+  }
+  goff.push_back((int32_t)steps.size());
   D.n_steps = (int32_t)steps.size();
 
   // ---- one device allocation: tables, then zeroed workspaces -------------------
@@ -246,6 +206,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const size_t o_pro = take(sizeof(DecProItem) * (size_t)n_pro + 16);
   const size_t o_vrows = take(sizeof(DecVeraRow) * 32 * (size_t)nvb + 16);
   const size_t o_steps = take(sizeof(DecStep) * steps.size() + 16);
+  const size_t o_goff = take(sizeof(int32_t) * goff.size());
   const size_t o_ones = take(4 * (size_t)d_out);
   const size_t tables = o;
   const size_t o_zeros = take(4 * (size_t)d_out);
@@ -380,6 +341,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   if (!pro.empty()) memcpy(h.data() + o_pro, pro.data(), sizeof(DecProItem) * pro.size());
   if (!vrows.empty()) memcpy(h.data() + o_vrows, vrows.data(), sizeof(DecVeraRow) * vrows.size());
   if (!steps.empty()) memcpy(h.data() + o_steps, steps.data(), sizeof(DecStep) * steps.size());
+  memcpy(h.data() + o_goff, goff.data(), sizeof(int32_t) * goff.size());
   for (int64_t j = 0; j < d_out; ++j) {
     const float one = 1.0f;
     memcpy(h.data() + o_ones + 4 * j, &one, 4);
@@ -401,6 +363,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   D.pro_items = (const DecProItem*)(d + o_pro);
   D.vrows = B->n_vera ? (const DecVeraRow*)(d + o_vrows) : nullptr;
   D.steps = (const DecStep*)(d + o_steps);
+  D.goff = (const int32_t*)(d + o_goff);
   D.zeros = zeros;
   D.xs = (uint16_t*)(d + o_xs);
   D.acc32[0] = (float*)(d + o_acc0);
