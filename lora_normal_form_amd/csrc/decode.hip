@@ -697,21 +697,29 @@ k_decode_main(MainArgs a) {
   // ---- epilogue ---------------------------------------------------------------
   // the first expand batch's operands and the rows' factor vectors are in
   // flight while the K halves meet
-  const int64_t ncol0 = (int64_t)c * 64 + m;
-  constexpr int NB = MGT <= 5 ? 8 : 4;  // register room
-  StepBatch<NB> sb;
-  load_batch(a, win, g_e0, g_e1, wave, ncol0, m, h, sb);
+  // (the e and b vectors first: their row records come from LDS, and with
+  // the batch's registers not yet taken the reads overlap)
   if constexpr (!s_early) issue_s();
   constexpr bool early_f = MGT <= 6;       // register room to fetch e and b here too
   f32x4 e4[2 * MGT], b4[2 * MGT];
   if constexpr (early_f) {
+    u32x4 re[2 * MGT], rb[2 * MGT];
 #pragma unroll
     for (int j = 0; j < 2 * MGT; ++j) {
       const int r = rr + 16 * min(j, nj - 1);
-      e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
-      b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
+      re[j] = rec[r][0];
+      rb[j] = rec[r][1];
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * MGT; ++j) {
+      e4[j] = ldg4(rec_ptr(re[j], 1) + cbase);
+      b4[j] = ldg4((kc == 0 ? rec_ptr(rb[j], 0) : a.zeros) + cbase);
     }
   }
+  const int64_t ncol0 = (int64_t)c * 64 + m;
+  constexpr int NB = MGT <= 5 ? 8 : 4;  // register room
+  StepBatch<NB> sb;
+  load_batch(a, win, g_e0, g_e1, wave, ncol0, m, h, sb);
 
   // (a) K halves meet in T [32 MGT rows][64 columns]; accumulator element i
   //     of group g is row 32 g + 8 (i / 4) + 4 h + i % 4, column cb 32 + m
