@@ -643,11 +643,16 @@ k_decode_main(MainArgs a) {
   const int64_t cbase = (int64_t)c * 64 + 4 * q4;
   f32x4 s4[2 * MGT];
   auto issue_s = [&]() {
+    // the s pointers (first 8 bytes of each record) read together, then the
+    // vectors, so the LDS reads overlap
+    const float* sp[2 * MGT];
 #pragma unroll
     for (int j = 0; j < 2 * MGT; ++j) {
       const int r = rr + 16 * min(j, nj - 1);
-      s4[j] = ldg4(rec_ptr(rec[r][0], 0) + cbase);
+      sp[j] = *reinterpret_cast<const float* const*>(&rec[r][0]);
     }
+#pragma unroll
+    for (int j = 0; j < 2 * MGT; ++j) s4[j] = ldg4(sp[j] + cbase);
   };
   constexpr bool s_early = NST >= 2;
 
@@ -802,11 +807,18 @@ k_decode_main(MainArgs a) {
   f32x4 out[2 * MGT];
   {
     if constexpr (!early_f) {
+      // (records read together first, so the LDS reads overlap)
+      u32x4 re[2 * MGT], rb[2 * MGT];
 #pragma unroll
       for (int j = 0; j < 2 * MGT; ++j) {
         const int r = rr + 16 * min(j, nj - 1);
-        e4[j] = ldg4(rec_ptr(rec[r][0], 1) + cbase);
-        b4[j] = ldg4((kc == 0 ? rec_ptr(rec[r][1], 0) : a.zeros) + cbase);
+        re[j] = rec[r][0];
+        rb[j] = rec[r][1];
+      }
+#pragma unroll
+      for (int j = 0; j < 2 * MGT; ++j) {
+        e4[j] = ldg4(rec_ptr(re[j], 1) + cbase);
+        b4[j] = ldg4((kc == 0 ? rec_ptr(rb[j], 0) : a.zeros) + cbase);
       }
     }
 #pragma unroll
