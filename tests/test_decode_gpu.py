@@ -184,3 +184,22 @@ def test_decode_dense_vera_matches_steps(shape):
     _, ys = _forward(wl, expect_path=1, SCUTE_DECODE_DENSE_VERA=0)
     _check(wl, ys, ref)
     assert np.max(np.abs(yd - ys)) <= 1e-3 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("d_out", [1024, 14336])
+def test_decode_many_expand_steps_per_row_group(d_out):
+    # every row its own adapter: 40 LoRA and 8 DoRA of rank 64 (4 expand steps
+    # of 16 ranks each) and 16 VeRA rows (r_v 256: 16 steps per row group), so
+    # a row group's step list in one K slice holds ~70 (two slices, 1024
+    # columns) to ~150 (one slice, 14336 columns) steps: several operand
+    # batches per wave and, at 14336 columns, a second descriptor window
+    _need_gpu()
+    ads = ([AdapterSpec("lora", rank=64) for _ in range(40)] +
+           [AdapterSpec("dora", rank=64) for _ in range(8)] +
+           [AdapterSpec("vera") for _ in range(16)])
+    n = 64
+    ta = np.arange(n) % len(ads)
+    wl = make_workload(WorkloadSpec(f"decode_many_steps_{d_out}", "bf16", 512, d_out, n, ads,
+                                    vera_rank=256, assign="explicit", token_adapter=ta, seed=51))
+    _, y = _forward(wl, expect_path=1)
+    _check(wl, y)
