@@ -14,8 +14,11 @@ streams its bytes from HBM rather than from the cache.
 
 Prints ONE JSON line. Also reports the roofline of the dominant kernel
 (algorithmic bytes per launch / its mean launch time from HIP events), the
-CPU oracle timed on the host, and the mixed-method overhead against the
-all-LoRA workload (4096 -> 4096, 128 tokens over 64 LoRA r16 adapters).
+CPU oracle timed on the host, and the mixed-method overhead two ways: against
+the all-LoRA workload (4096 -> 4096, 128 tokens over 64 LoRA r16 adapters),
+and against a matched batch with the mixed workload's token assignment where
+every one of its 40 adapters is LoRA r16 (the same number of adapters, as the
+explainer's mixed-pool comparison has it).
 """
 
 import argparse
@@ -153,6 +156,16 @@ def calib_copy(torch, mib):
     torch.cuda.synchronize()
 
 
+def matched_lora(wl):
+    """The same batch (shape, tokens, token -> adapter assignment, seed) with
+    every adapter replaced by a LoRA adapter of rank 16 (c = 2)."""
+    from synth import AdapterSpec, WorkloadSpec, make_workload
+    ads = [AdapterSpec("lora", rank=16, c=2.0) for _ in wl.adapters]
+    return make_workload(WorkloadSpec(wl.name + "_matched_lora_r16", wl.dtype, wl.d_in, wl.d_out,
+                                      wl.n, ads, assign="explicit",
+                                      token_adapter=wl.token_adapter, seed=wl.seed))
+
+
 def cpu_baseline(wl, seconds):
     import numpy as np
     import oracle
@@ -253,6 +266,15 @@ def main():
         extra["all_lora_gbps"] = round(m1["cost"]["bytes"] / (ms1 * 1e-3) / 1e9, 1)
         extra["mixed_over_all_lora_time"] = round(ms / ms1, 4)
         del m1
+        print("bench: matched all-LoRA batch (same assignment, 40 x LoRA r16)", file=sys.stderr,
+              flush=True)
+        wlm = matched_lora(wl)
+        m2 = measure(torch, wlm, args.steps, args.warmup)
+        ms2 = m2["gpu_ms"] / args.steps
+        extra["matched_lora_us"] = round(ms2 * 1e3, 3)
+        extra["matched_lora_gbps"] = round(m2["cost"]["bytes"] / (ms2 * 1e-3) / 1e9, 1)
+        extra["mixed_over_matched_lora_time"] = round(ms / ms2, 4)
+        del m2
 
     if args.calib_copy > 0:
         calib_copy(torch, args.calib_copy)

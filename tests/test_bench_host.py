@@ -1,0 +1,31 @@
+"""Host-side checks of bench.py (no GPU): the matched all-LoRA comparison
+batch, and the refusal of more than one GPU."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from synth import make_config  # noqa: E402
+
+
+def test_matched_lora_keeps_the_batch_and_replaces_every_adapter():
+    wl = make_config(2)
+    m = bench.matched_lora(wl)
+    assert (m.n, m.d_in, m.d_out, m.dtype) == (wl.n, wl.d_in, wl.d_out, wl.dtype)
+    assert np.array_equal(m.token_adapter, wl.token_adapter)
+    assert np.array_equal(m.x, wl.x) and np.array_equal(m.W, wl.W)
+    assert len(m.adapters) == len(wl.adapters)
+    assert all(a.method == "lora" and a.rank == 16 for a in m.adapters)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
