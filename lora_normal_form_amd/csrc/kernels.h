@@ -74,12 +74,6 @@ __device__ __forceinline__ uint4 ldb16(rsrc_t r, uint32_t off) {
 // with an atomic on a counter; a reader issues its loads only after the
 // atomic that saw every announcement has returned.
 constexpr int CPOL_SYS = 17;  // sc0 | sc1
-__device__ __forceinline__ void st_sys(rsrc_t r, uint32_t off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CPOL_SYS);
-}
-__device__ __forceinline__ float ld_sys(rsrc_t r, uint32_t off) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_SYS));
-}
 __device__ __forceinline__ void st_sys4(rsrc_t r, uint32_t off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, CPOL_SYS);
 }
