@@ -211,6 +211,51 @@ __device__ __forceinline__ void pf_steps(const PfSrc& src, uint8_t* s0, uint8_t*
   }
 }
 
+// Consumer side of the producer-wave K loop: step T waits at the work-group
+// barrier (the producer wave has waited for stage T's loads before it, and
+// every consumer is done with stage T - 1) and multiplies stage T; the
+// consumers issue no loads, so a full load queue never holds up an MFMA.
+template <int NST, int T>
+__device__ __forceinline__ void pf_csteps(uint8_t* s0, uint8_t* s1, uint8_t* s2,
+                                          f32x16 (&acc)[4][2], int m, int h, int w) {
+  if constexpr (T < NST) {
+    uint8_t* cur = T % 3 == 0 ? s0 : (T % 3 == 1 ? s1 : s2);
+    wg_barrier();
+    pf_mma<false>(cur, acc, m, h, w);
+    pf_csteps<NST, T + 1>(s0, s1, s2, acc, m, h, w);
+  }
+}
+// Producer wave: issues every direct-to-LDS load of the tile (the four
+// consumer waves' shares, `src[v]` for consumer v), two stages ahead; before
+// the barrier of step T it waits for stage T (stage T + 1 may be in flight),
+// after it refills the slot stage T - 1 used with stage T + 2.
+constexpr int PF_STAGE_LOADS = 4 * PF_LOADS;  // loads the producer issues per stage
+__device__ __forceinline__ void pf_produce(const PfSrc (&src)[4], uint8_t* s0, uint8_t* s1,
+                                           uint8_t* s2, int nst) {
+  issue_fence();
+#pragma unroll
+  for (int v = 0; v < 4; ++v) pf_stage(s0, src[v], 0, v);
+  if (nst > 1) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) pf_stage(s1, src[v], 1, v);
+  }
+  issue_fence();
+  for (int t = 0; t < nst; ++t) {
+    if (t + 1 < nst)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PF_STAGE_LOADS));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    wg_barrier();
+    if (t + 2 < nst) {
+      const int tn = t + 2;
+      uint8_t* nxt = tn % 3 == 0 ? s0 : (tn % 3 == 1 ? s1 : s2);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) pf_stage(nxt, src[v], tn, v);
+    }
+    issue_fence();
+  }
+}
+
 // the K loop over NST stages: the first two stages, then the pipeline steps
 template <int NST>
 __device__ __forceinline__ void pf_kloop(const PfSrc& src, uint8_t* s0, uint8_t* s1, uint8_t* s2,
@@ -235,8 +280,10 @@ __device__ __forceinline__ uint4 scale_bf8(uint4 v, float e) {
 
 // NST: stages of the whole K dimension (a K part of a split tile covers
 // NST / P of them)
+// Five waves: waves 0..3 multiply (and run the epilogue), wave 4 issues the
+// K loop's loads and leaves after the loop.
 template <int NST>
-__global__ void __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(320, 1)
 k_prefill_main(PfArgs a) {
   // ring slots as separate LDS objects, so the compiler can tell the slot
   // being read from the ones the direct loads fill
@@ -254,12 +301,32 @@ k_prefill_main(PfArgs a) {
   const int64_t d_in = a.d_in, d_out = a.d_out;
   const int64_t col0 = (int64_t)c * 256 + 64 * w + m;  // column block cb: col0 + 32 cb
   const PfChunk ch = a.chunks[ci];
-
-  // (1) row sources of this lane's 4 pieces per stage, its token-table entry
   const GLOBAL int32_t* cr = (const GLOBAL int32_t*)(a.crow + (size_t)ci * 128);
-  int32_t srow[4];
+
+  // (0) the producer wave: sources of every consumer's pieces, then the loads
+  if (w == 4) {
+    PfSrc srcv[4];
+    const bool rot = (__builtin_amdgcn_readfirstlane(ch.flags) & PF_ROT) != 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) srow[q] = cr[8 * w + 32 * q + (lane >> 3)];
+    for (int v = 0; v < 4; ++v) {
+      const int piece = (lane & 7) ^ ((4 * v + (lane >> 4)) & 7);
+      srcv[v].rlo = make_rsrc(a.x, a.x_bytes);
+      srcv[v].rhi = rot ? make_rsrc(a.dx, a.dx_bytes) : srcv[v].rlo;
+      srcv[v].rw = make_rsrc(a.W + (size_t)c * 256 * d_in, (uint32_t)(256 * d_in * 2));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int32_t r = cr[8 * v + 32 * q + (lane >> 3)];
+        srcv[v].roff[q] = (uint32_t)(((int64_t)(r >= 0 ? r : -r - 1) * d_in + 8 * piece) * 2);
+      }
+      srcv[v].woff = (uint32_t)(((int64_t)(8 * v + (lane >> 3)) * d_in + 8 * piece) * 2);
+      srcv[v].wstep = (uint32_t)(32 * d_in * 2);
+      srcv[v].kb = kp < 0 ? 0 : kp * (NST / a.P) * PK * 2;
+    }
+    pf_produce(srcv, slot0, slot1, slot2, kp < 0 ? NST : NST / a.P);
+    return;
+  }
+
+  // (1) this lane's token-table entry
   const int32_t tokv = cr[tid & 127];
   // (2) factor vectors of this lane's columns (used after the K loop)
   float sv[2], ev[2], bv[2];
@@ -269,24 +336,6 @@ k_prefill_main(PfArgs a) {
     ev[cb] = ldg(ch.e + col0 + 32 * cb);
     bv[cb] = ldg(ch.b + col0 + 32 * cb);
   }
-  // (3) sources, then the first two stages
-  PfSrc src;
-  {
-    const int piece = (lane & 7) ^ ((4 * w + (lane >> 4)) & 7);
-    const bool rot = (__builtin_amdgcn_readfirstlane(ch.flags) & PF_ROT) != 0;
-    src.rlo = make_rsrc(a.x, a.x_bytes);
-    src.rhi = rot ? make_rsrc(a.dx, a.dx_bytes) : src.rlo;
-    src.rw = make_rsrc(a.W + (size_t)c * 256 * d_in, (uint32_t)(256 * d_in * 2));
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int32_t v = srow[q];
-      src.roff[q] = (uint32_t)(((int64_t)(v >= 0 ? v : -v - 1) * d_in + 8 * piece) * 2);
-    }
-    src.woff = (uint32_t)(((int64_t)(8 * w + (lane >> 3)) * d_in + 8 * piece) * 2);
-    src.wstep = (uint32_t)(32 * d_in * 2);
-    src.kb = kp < 0 ? 0 : kp * (NST / a.P) * PK * 2;
-  }
-
   // (4) K loop: the whole K, or one of P parts
   f32x16 acc[4][2];
 #pragma unroll
@@ -294,11 +343,11 @@ k_prefill_main(PfArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[g][cb] = f32x16{};
   if (kp < 0)
-    pf_kloop<NST>(src, slot0, slot1, slot2, acc, m, h, w);
+    pf_csteps<NST, 0>(slot0, slot1, slot2, acc, m, h, w);
   else if (a.P == 4)
-    pf_kloop<NST / 4>(src, slot0, slot1, slot2, acc, m, h, w);
+    pf_csteps<NST / 4, 0>(slot0, slot1, slot2, acc, m, h, w);
   else
-    pf_kloop<NST / 2>(src, slot0, slot1, slot2, acc, m, h, w);
+    pf_csteps<NST / 2, 0>(slot0, slot1, slot2, acc, m, h, w);
   lds_barrier();  // every wave is done with the ring
 
   // (4b) the P parts of a split tile meet: each stores its partial tile with
@@ -765,7 +814,7 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
     return fail(SCUTE_E_STATE, "prefill path: plan tables missing");
   {
     ProfScope ps(L, st, "prefill_main");
-    hipLaunchKernelGGL(k_prefill_main<64>, dim3(P.n_items), dim3(256), 0, st, ma);
+    hipLaunchKernelGGL(k_prefill_main<64>, dim3(P.n_items), dim3(320), 0, st, ma);
     ++nl;
   }
   hipError_t e = hipGetLastError();
