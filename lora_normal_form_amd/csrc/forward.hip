@@ -139,34 +139,35 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
                                                   const SlotEntry* __restrict__ table, int32_t n,
                                                   int32_t n_rot, int64_t d_in, int64_t d_out,
                                                   float* __restrict__ y) {
-  __shared__ float xs[32][33];
-  __shared__ float ws[32][33];
+  // 128 k per round: every thread's 32 loads of a round are in flight
+  // together, so a round costs one memory round trip
+  constexpr int KR = 128;
+  __shared__ float xs[32][KR + 1];
+  __shared__ float ws[32][KR + 1];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int32_t p0 = blockIdx.y * 32;
   const int64_t j0 = (int64_t)blockIdx.x * 32;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const int passes = (p0 < n_rot) ? 2 : 1;
   for (int pass = 0; pass < passes; ++pass) {
-    for (int64_t k0 = 0; k0 < d_in; k0 += 32) {
+    for (int64_t k0 = 0; k0 < d_in; k0 += KR) {
       for (int q = 0; q < 4; ++q) {
         const int r = ty + 8 * q;
         const int32_t p = p0 + r;
-        const int64_t kk = k0 + tx;
-        float xv = 0.f;
-        if (kk < d_in) {
-          if (pass == 0) {
-            if (p < n) xv = ldf(x, (size_t)perm[p] * d_in + kk);
-          } else {
-            if (p < n_rot) xv = ldf(delta, (size_t)p * d_in + kk);
-          }
-        }
-        xs[r][tx] = xv;
         const int64_t j = j0 + r;
-        ws[r][tx] = (j < d_out && kk < d_in) ? ldf(W, (size_t)j * d_in + kk) : 0.f;
+        const bool xrow = pass == 0 ? p < n : p < n_rot;
+        const T* xsrc = pass == 0 ? (p < n ? x + (size_t)perm[p] * d_in : x)
+                                  : delta + (size_t)min(p, max(n_rot - 1, 0)) * d_in;
+#pragma unroll
+        for (int cq = 0; cq < KR / 32; ++cq) {
+          const int64_t kk = k0 + 32 * cq + tx;
+          xs[r][32 * cq + tx] = (xrow && kk < d_in) ? ldf(xsrc, kk) : 0.f;
+          ws[r][32 * cq + tx] = (j < d_out && kk < d_in) ? ldf(W, (size_t)j * d_in + kk) : 0.f;
+        }
       }
       __syncthreads();
 #pragma unroll 8
-      for (int kk = 0; kk < 32; ++kk) {
+      for (int kk = 0; kk < KR; ++kk) {
         const float wv = ws[tx][kk];
         for (int q = 0; q < 4; ++q) acc[q] += xs[ty + 8 * q][kk] * wv;
       }
