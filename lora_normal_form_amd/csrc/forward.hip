@@ -142,8 +142,10 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
   // 128 k per round: every thread's 32 loads of a round are in flight
   // together, so a round costs one memory round trip
   constexpr int KR = 128;
-  __shared__ float xs[32][KR + 1];
-  __shared__ float ws[32][KR + 1];
+  // rows padded to 132 floats: 16-byte aligned for the float4 reads below,
+  // and 8 consecutive rows start in 8 different 4-bank groups
+  __shared__ __attribute__((aligned(16))) float xs[32][KR + 4];
+  __shared__ __attribute__((aligned(16))) float ws[32][KR + 4];
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   const int32_t p0 = blockIdx.y * 32;
   const int64_t j0 = (int64_t)blockIdx.x * 32;
@@ -166,10 +168,19 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
         }
       }
       __syncthreads();
-#pragma unroll 8
-      for (int kk = 0; kk < KR; ++kk) {
-        const float wv = ws[tx][kk];
-        for (int q = 0; q < 4; ++q) acc[q] += xs[ty + 8 * q][kk] * wv;
+      // 4 k per step: one float4 of W and one of each of the 4 rows (16 FMAs
+      // per 5 LDS reads)
+#pragma unroll 4
+      for (int kk = 0; kk < KR; kk += 4) {
+        const float4 wv = *reinterpret_cast<const float4*>(&ws[tx][kk]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 xv = *reinterpret_cast<const float4*>(&xs[ty + 8 * q][kk]);
+          acc[q] += xv.x * wv.x;
+          acc[q] += xv.y * wv.y;
+          acc[q] += xv.z * wv.z;
+          acc[q] += xv.w * wv.w;
+        }
       }
       __syncthreads();
     }
