@@ -243,6 +243,11 @@ struct DecCfg {
   static constexpr int PER_STAGE = 4 + 2 * MGT;
   // outstanding loads allowed when waiting for stage t (see the loop)
   static constexpr int WAIT = (R - 2) * PER_STAGE + 4;
+  // W loads whole rows per instruction and passes through a 4 KB LDS block
+  // per wave when that block fits beside the ring and the row records (with
+  // the 3-deep ring only: with 2 slots, as on the FFN-up shape, it measured
+  // slower)
+  static constexpr bool WLDS = R == 3 && R * 2 * STAGE + 4 * 4096 + 32 * MGT * 32 + 1024 <= 160 * 1024;
 };
 
 
@@ -261,24 +266,46 @@ __device__ __forceinline__ void stage_rows(uint8_t* stage, const uint16_t* const
                                      (lds_void*)(stage + (cb + 2 * q) * 1024), 16, 0, 0);
 }
 
-// W of one stage for this lane: 64 contiguous bytes of its W row, addressed
-// by a fixed per-lane buffer offset plus the stage's scalar offset (no
-// per-load address registers)
+// W of one stage for one wave: 32 W rows (the wave's columns) x 128 bytes
+// (64 k), addressed by a fixed per-lane buffer offset plus the stage's
+// scalar offset. Two lane layouts:
+//  - direct (rstep = 16 bytes): lane (m, h) loads the 64 contiguous bytes of its
+//    own row m that it multiplies (pieces 4h .. 4h+3); each instruction then
+//    touches 32 rows;
+//  - through LDS (rstep = 8 rows): instruction s, lane l loads row
+//    8 s + l / 8, piece (l % 8) ^ (l / 8), so one instruction covers 8 whole
+//    rows; the wave writes the four registers to its LDS block in lane order
+//    (row r's piece p lands in slot p ^ (r % 8)) and reads back the
+//    direct layout, bank-conflict free.
 struct WSrc {
   rsrc_t r;
-  uint32_t voff;
+  uint32_t voff, rstep;
+  uint8_t* wsw;  // the wave's 4 KB LDS block (through-LDS layout)
 };
 __device__ __forceinline__ void load_w(uint4 (&wr)[4], const WSrc& ws, int64_t koff) {
   const int soff = (int)(koff * 2);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    wr[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ws.r, ws.voff + 16 * s, soff, 0));
+    wr[s] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(ws.r, ws.voff + s * ws.rstep, soff, 0));
 }
 
 // one stage: 4 MFMA k-steps of 16 over every staged row group
 template <int MGT>
-__device__ __forceinline__ void mma_stage(const uint8_t* stage, const uint4 (&wr)[4],
+__device__ __forceinline__ void mma_stage(const uint8_t* stage, const uint4 (&wl)[4], const WSrc& ws,
                                           f32x16 (&acc)[MGT], int m, int h) {
+  uint4 wr[4];
+  if constexpr (DecCfg<MGT>::WLDS) {
+    // through the wave's LDS block: the wave's own writes and reads, in order
+#pragma unroll
+    for (int s = 0; s < 4; ++s) *reinterpret_cast<uint4*>(ws.wsw + s * 1024 + (32 * h + m) * 16) = wl[s];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      wr[s] = *reinterpret_cast<const uint4*>(ws.wsw + m * 128 + 16 * ((4 * h + s) ^ (m & 7)));
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) wr[s] = wl[s];
+  }
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     uint4 av[MGT];
@@ -306,7 +333,7 @@ __device__ __forceinline__ void kstep(int t, int nst, const WSrc& wrow,
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(DecCfg<MGT>::WAIT));
   wg_barrier();
   stage_rows<MGT>(nxt + kp * DecCfg<MGT>::STAGE, src, kn, cb);
-  mma_stage<MGT>(cur + kp * DecCfg<MGT>::STAGE, wc, acc, m, h);
+  mma_stage<MGT>(cur + kp * DecCfg<MGT>::STAGE, wc, wrow, acc, m, h);
 }
 
 // The same step with the stage index T known at compile time: W is
@@ -340,7 +367,7 @@ __device__ __forceinline__ void ksteps_static(const WSrc& wrow, const uint16_t* 
       issue_fence();
     }
     if constexpr (TN < NST) stage_rows<MGT>(nxt + kp * Cfg::STAGE, src, (int64_t)SK * TN, cb);
-    mma_stage<MGT>(cur + kp * Cfg::STAGE, wb[T % (LW + 1)], acc, m, h);
+    mma_stage<MGT>(cur + kp * Cfg::STAGE, wb[T % (LW + 1)], wrow, acc, m, h);
     ksteps_static<MGT, NST, LW, T + 1, NE>(wrow, src, s0, s1, s2, wb, acc, m, h, cb, kp, early);
   }
 }
@@ -570,6 +597,7 @@ k_decode_main(MainArgs a) {
   __shared__ u32x4 rec[32 * MGT][2];   // row records of the x rows
   __shared__ int32_t vflag[MGT];       // V holds the group's VeRA product
   __shared__ int32_t last_flag;
+  __shared__ __attribute__((aligned(1024))) uint8_t wst[Cfg::WLDS ? 4 * 4096 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
@@ -587,8 +615,13 @@ k_decode_main(MainArgs a) {
   const int kw = a.k_chunk / 2;  // K per half
   const int64_t kbase = (int64_t)kc * a.k_chunk + (int64_t)kp * kw;
   const int nst = NST > 0 ? NST : kw / SK;
-  const WSrc wrow{make_rsrc(a.W, (uint32_t)((size_t)a.d_out * a.d_in * 2)),
-                  (uint32_t)(((size_t)ncol * a.d_in + kbase + 32 * h) * 2)};
+  const rsrc_t wr_rsrc = make_rsrc(a.W, (uint32_t)((size_t)a.d_out * a.d_in * 2));
+  const WSrc wrow =
+      Cfg::WLDS ? WSrc{wr_rsrc,
+                       (uint32_t)((((size_t)c * 64 + cb * 32 + (lane >> 3)) * a.d_in + kbase) * 2 +
+                                  16 * ((lane & 7) ^ (lane >> 3))),
+                       (uint32_t)(8 * a.d_in * 2), wst + (Cfg::WLDS ? wave * 4096 : 0)}
+                : WSrc{wr_rsrc, (uint32_t)(((size_t)ncol * a.d_in + kbase + 32 * h) * 2), 16u, wst};
 
   // (0) record of the row this thread keeps for the epilogue
   // (branch-free, so the compiler can fetch the kernel arguments at once)
@@ -672,7 +705,7 @@ k_decode_main(MainArgs a) {
     }
     if (tid < MGT) vflag[tid] = 0;
     if constexpr (pre) stage_rows<MGT>((R == 3 ? slot2 : slot1) + kp * Cfg::STAGE, src, kn, cb);
-    mma_stage<MGT>(slot0 + kp * Cfg::STAGE, wb[0], acc, m, h);
+    mma_stage<MGT>(slot0 + kp * Cfg::STAGE, wb[0], wrow, acc, m, h);
   }
   // remaining stages; stage t lives in ring slot t % R and W registers
   // wb[t % R], named statically in both forms of the loop
