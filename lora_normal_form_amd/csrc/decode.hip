@@ -69,7 +69,7 @@ __device__ __forceinline__ void rotate_rows(const uint16_t* Pt, int32_t blk,
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int q = 0; q < CH / 8; ++q) acc[r] += dot8(xv[r][q], pv[q]);
+      for (int q = 0; q < CH / 8; ++q) acc[r] = dot8(xv[r][q], pv[q], acc[r]);
   }
 }
 
@@ -188,7 +188,7 @@ k_decode_prologue(ProArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[r][j] += dot8(xv[cc][r], av[cc][j]);
+            for (int j = 0; j < 4; ++j) acc[r][j] = dot8(xv[cc][r], av[cc][j], acc[r][j]);
       }
       float mine = 0.f;
 #pragma unroll

@@ -39,15 +39,16 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
 }
 __device__ __forceinline__ f32x4 ldg4(const float* p) { return *(const GLOBAL f32x4*)p; }
 __device__ __forceinline__ void stg4(float* p, f32x4 v) { *(GLOBAL f32x4*)p = v; }
-__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+// c + the dot product of 8 bf16 pairs, on four bf16 dot2 instructions
+// (fp32 accumulate)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8(uint4 a, uint4 b, float c) {
   const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-  float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s += __uint_as_float(av[i] << 16) * __uint_as_float(bv[i] << 16);
-    s += __uint_as_float(av[i] & 0xFFFF0000u) * __uint_as_float(bv[i] & 0xFFFF0000u);
-  }
-  return s;
+  for (int i = 0; i < 4; ++i)
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, av[i]),
+                                        __builtin_bit_cast(bf16x2_t, bv[i]), c, false);
+  return c;
 }
 __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
