@@ -22,7 +22,8 @@
 // one of S slices of K for all rows of the batch:
 //   base     x W and delta W on 32x32x16 bf16 MFMA: x / delta rows staged in
 //            LDS by direct global->LDS loads through a ring of 64-k stages,
-//            W streamed straight into registers;
+//            W streamed into registers (through a per-wave LDS block that
+//            turns whole-row loads into the MFMA layout where LDS allows);
 //   epilogue the accumulators move to an LDS tile. Row-wise passes (16
 //            threads per row, so each row's factor vectors are read through
 //            a row-uniform pointer with coalesced 16-byte accesses) fold
@@ -232,7 +233,7 @@ struct MainArgs {
 // Tile of the main kernel: 64 output columns (two 32-column MFMA blocks) by
 // one of S slices of K; the 4 waves of a work-group are (column block cb,
 // K half kp). The x / delta rows of each K half stream through an LDS ring
-// of R stages of 64 k; W streams straight into registers.
+// of R stages of 64 k; W streams into registers (see WSrc).
 constexpr int SK = 64;                 // k per stage
 constexpr int SROW = 2 * SK;           // bytes per staged row
 template <int MGT>

@@ -10,8 +10,8 @@
         scaled by the factor that maps its reading for a plain device copy of
         N MiB (the runtime's copy kernel, launched by bench.py --calib-copy N)
         to the N MiB it actually read and wrote. The JSON records the SHA-256
-        of the kernel sources, and bench.py uses the figures only while the
-        sources are unchanged.
+        of the kernel sources' code (comments removed), and bench.py uses the
+        figures only while that code is unchanged.
 """
 
 from __future__ import annotations
@@ -29,15 +29,44 @@ KERNEL_SOURCES = ["csrc/decode.hip", "csrc/forward.hip", "csrc/prefill.hip", "cs
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+def strip_comments(src: str) -> str:
+    """C++ source without its comments and blank lines, each line's runs of
+    blanks collapsed (string and character literals otherwise kept as they
+    are), so that edits to comments or layout alone leave the hash of the
+    code unchanged."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (" ".join(ln.split()) for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_sha() -> str:
-    """SHA-256 over the HIP kernel sources (those that exist)."""
+    """SHA-256 over the code of the HIP kernel sources (those that exist),
+    comments removed."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         path = os.path.join(PKG, rel)
         if os.path.exists(path):
             h.update(rel.encode())
-            with open(path, "rb") as f:
-                h.update(f.read())
+            with open(path, encoding="utf-8") as f:
+                h.update(strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

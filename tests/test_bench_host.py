@@ -29,3 +29,13 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_counter_sources_hash_ignores_comments_only():
+    from lora_normal_form_amd.profsum import strip_comments
+    code = 'int a = 1;  // one\n/* block\n   comment */\nconst char* s = "x // y /* z */";\nchar q = \'"\';\n'
+    recommented = 'int a = 1;  // first\n// added line\nconst char* s = "x // y /* z */";\n/* another */ char q = \'"\';\n'
+    assert strip_comments(code) == strip_comments(recommented)
+    # literals that look like comments stay, and a change of code is seen
+    assert '"x // y /* z */"' in strip_comments(code)
+    assert strip_comments(code) != strip_comments(code.replace("a = 1", "a = 2"))
