@@ -10,7 +10,7 @@
 //               stored after the sorted x rows;
 //   own shrink  t = x A' for up to 4 rows x 4 ranks over a K part of 1024;
 //   VeRA shrink u = (x A_sh) (.) d for 32 VeRA rows x 32 ranks over a K
-//               slice of 256, on one 32x32x16 MFMA tile.
+//               slice of 256, on four 16x16x32 MFMA tiles.
 // Rotation runs before the shared GEMM and the shared VeRA pair is read once
 // per step for the whole batch ("Where is the cheapest place to compute the
 // remaining slots?", paper-daily.com explainer of "Scute: Exact Batched
@@ -94,24 +94,63 @@ k_decode_prologue(ProArgs a) {
       const int32_t per_kv = a.nvb * a.njb;
       const int32_t kv = it / per_kv, vb = (it - kv * per_kv) / a.njb;
       const int32_t jb = it - kv * per_kv - vb * a.njb;
-      const int m = lane & 31, h = lane >> 5;
-      const DecVeraRow vr = a.vrows[32 * vb + m];
-      const uint16_t* xr = a.x + (size_t)vr.tok * d_in + (int64_t)kv * 256 + 32 * h;
-      const uint16_t* ar = a.A_sh + (size_t)(32 * jb + m) * d_in + (int64_t)kv * 256 + 32 * h;
-      // output element i: VeRA row 32 vb + 8 (i / 4) + 4 h + i % 4, rank 32 jb + m
-      const int32_t j = 32 * jb + m;
-      float dsc[16];
-      int32_t prow[16];
+      // 16x16x32 MFMA tiles (2 x 2 of them): lane (i, g) = (lane % 16,
+      // lane / 16) holds row i of a 16-row block, k 8 g .. 8 g + 7 of each
+      // 32-k step. Step ks takes the 64-byte half (ks % 2) of the 128-byte
+      // chunk ks / 2 on both operands, so one load instruction covers 16 rows
+      // x 64 contiguous bytes.
+      const int i16 = lane & 15, g = lane >> 4;
+      const DecVeraRow v0 = a.vrows[32 * vb + i16], v1 = a.vrows[32 * vb + 16 + i16];
+      const int64_t kof = (int64_t)kv * 256 + 8 * g;
+      const uint16_t* xr[2] = {a.x + (size_t)v0.tok * d_in + kof, a.x + (size_t)v1.tok * d_in + kof};
+      const uint16_t* ar[2] = {a.A_sh + (size_t)(32 * jb + i16) * d_in + kof,
+                               a.A_sh + (size_t)(32 * jb + 16 + i16) * d_in + kof};
+      // output (bi, bj) element t: VeRA row 32 vb + 16 bi + 4 g + t,
+      // rank 32 jb + 16 bj + i16
+      float dsc[2][4][2];
+      int32_t prow[2][4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const DecVeraRow o = a.vrows[32 * vb + 8 * (i >> 2) + 4 * h + (i & 3)];
-        prow[i] = o.p;
-        dsc[i] = ldg(o.vd + j);
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const DecVeraRow o = a.vrows[32 * vb + 16 * bi + 4 * g + t];
+          prow[bi][t] = o.p;
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj) dsc[bi][t][bj] = ldg(o.vd + 32 * jb + 16 * bj + i16);
+        }
+      uint4 xa[2][8], wa[2][8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = 64 * (ks >> 1) + 32 * (ks & 1);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          xa[b][ks] = ldg16(xr[b] + off);
+          wa[b][ks] = ldg16(ar[b] + off);
+        }
       }
-      const f32x16 acc = shrink_tile(xr, ar);
+      f32x4 c[2][2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + a.RT + j, acc[i] * dsc[i]);
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) c[bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj)
+            c[bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_frag(xa[bi][ks]), as_frag(wa[bj][ks]),
+                                                               c[bi][bj], 0, 0, 0);
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (prow[bi][t] >= 0) {
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+              atomicAdd(a.acc + (size_t)prow[bi][t] * a.AW + a.RT + 32 * jb + 16 * bj + i16,
+                        c[bi][bj][t] * dsc[bi][t][bj]);
+          }
       continue;
     }
     const DecProItem item = a.items[it];
