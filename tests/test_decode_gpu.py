@@ -108,6 +108,19 @@ def test_decode_path_256_rows_few_rotated():
     _check(wl, y)
 
 
+@pytest.mark.parametrize("splitk", [1, 2])
+def test_decode_long_k_slices_with_w_through_lds(splitk):
+    # d_in 4096 in one slice (32 stages of 64 k per K half, the loop unrolled
+    # at compile time) or two (16 stages, the runtime loop), with at most 5
+    # staged row groups, where W passes through each wave's LDS block
+    _need_gpu()
+    wl = _wl(100, seed=61, d_in=4096, d_out=1024)
+    ld, y = _forward(wl, expect_path=1, SCUTE_DECODE_SPLITK=splitk)
+    info = ld.batch.info()
+    assert -(-wl.n // 32) + -(-info["n_rot_rows"] // 32) <= 5, info
+    _check(wl, y)
+
+
 @pytest.mark.parametrize("splitk", [1, 2, 4])
 def test_decode_path_split_k(splitk):
     # S = 1 stores y directly; S > 1 adds partial products with atomics
