@@ -360,3 +360,72 @@ def test_effect_error_hand_example():
     assert e == {0: pytest.approx(0.1 / 2.0)}
     ok, err, scale = oracle.max_error_ok(y, ref, 0.1)
     assert ok and err == pytest.approx(0.5) and scale == 6.0
+
+
+def _grid(n=4, d=5):
+    # a reference with max |ref| = 10 exactly (one entry), base = ref minus a
+    # known per-row effect
+    ref = np.full((n, d), 2.0)
+    ref[0, 0] = 10.0
+    base = ref.copy()
+    base[:, 1] -= 1.0          # every row's effect: 1.0 in column 1, so sum = d-independent
+    return ref, base
+
+
+def test_check_fp32_threshold_is_1e4_of_max():
+    ref, base = _grid()
+    ta = np.array([0, 0, 1, 1])
+    y = ref.copy()
+    y[2, 3] += 1.5e-3          # 1.5e-4 * max|ref| (=10): fails the fp32 bar
+    ok, rep = oracle.check(y, ref, base, ta, "f32")
+    assert not ok and rep["tol"] == 1e-4 and rep["max_abs_ref"] == 10.0
+    y[2, 3] = ref[2, 3] + 0.9e-3   # 0.9e-4 * max: passes
+    ok, _ = oracle.check(y, ref, base, ta, "f32")
+    assert ok
+    y[2, 3] = ref[2, 3] + 1.0e-3   # exactly at the bar: passes (<=)
+    ok, _ = oracle.check(y, ref, base, ta, "f32")
+    assert ok
+
+
+def test_check_bf16_max_error_threshold_is_1e2_of_max():
+    ref, base = _grid()
+    ta = np.array([-1, -1, -1, -1])    # no adapters: only the max criterion grades
+    y = ref.copy()
+    y[1, 4] += 0.09            # 0.9e-2 * max: passes
+    ok, rep = oracle.check(y, ref, base, ta, "bf16")
+    assert ok and rep["tol"] == 1e-2
+    y[1, 4] = ref[1, 4] + 0.11     # 1.1e-2 * max: fails
+    ok, _ = oracle.check(y, ref, base, ta, "bf16")
+    assert not ok
+
+
+def test_check_bf16_effect_threshold_is_one_percent():
+    ref, base = _grid()
+    ta = np.array([0, 0, 1, 1])
+    # adapter 1's effect is sum |ref - base| over rows 2, 3 = 2.0; an absolute
+    # error of 0.022 there is 1.1% of it (far below the max-error bar of 0.1)
+    y = ref.copy()
+    y[3, 2] += 0.022
+    ok, rep = oracle.check(y, ref, base, ta, "bf16")
+    assert rep["max_ok"] and not rep["effect_ok"] and not ok
+    assert rep["worst_effect_err"] == pytest.approx(0.011)
+    y[3, 2] = ref[3, 2] + 0.018    # 0.9% of its effect: passes
+    ok, rep = oracle.check(y, ref, base, ta, "bf16")
+    assert ok and rep["worst_effect_err"] == pytest.approx(0.009)
+
+
+def test_check_zero_effect_adapter_is_reported_not_graded():
+    # adapter 2 changes nothing (ref == base on its rows): its effect error
+    # is undefined, so it is reported and left to the max-error criterion
+    ref, base = _grid()
+    base[3] = ref[3]
+    ta = np.array([0, 0, 1, 2])
+    y = ref.copy()
+    y[3, 0] += 0.05            # inside the 1e-2 * max bar
+    e = oracle.effect_errors(y, ref, base, ta)
+    assert np.isnan(e[2]) and e[0] == 0.0 and e[1] == 0.0
+    ok, rep = oracle.check(y, ref, base, ta, "bf16")
+    assert ok and rep["zero_effect_adapters"] == [2] and rep["worst_effect_err"] == 0.0
+    y[3, 0] = ref[3, 0] + 0.2  # beyond the max-error bar: fails through that criterion
+    ok, rep = oracle.check(y, ref, base, ta, "bf16")
+    assert not ok and not rep["max_ok"]
