@@ -86,3 +86,35 @@ def test_dora_magnitude_near_column_norm():
 
 def test_names():
     assert len(CONFIG_NAMES) == 5
+
+
+@pytest.mark.parametrize("idx", range(5))
+def test_generator_digests_pinned(idx):
+    # every array of the five named workloads hashes to its committed digest
+    # (tests/golden/generator_sha256.json, written by generator_digests.py)
+    import json
+    import os
+    import sys
+    golden = os.path.join(os.path.dirname(__file__), "golden")
+    sys.path.insert(0, golden)
+    try:
+        import generator_digests as gd
+    finally:
+        sys.path.remove(golden)
+    with open(os.path.join(golden, "generator_sha256.json")) as f:
+        want = json.load(f)[str(idx)]
+    got = gd.digests(idx)
+    assert got == want
+
+
+def test_digest_catches_draw_order_change():
+    # swapping two draws (x drawn after W) changes the x digest: the pin is
+    # sensitive to draw order, not only to the multiset of values
+    import hashlib
+    rng = np.random.default_rng(np.random.PCG64(1001))
+    x1 = rng.standard_normal(16)
+    rng = np.random.default_rng(np.random.PCG64(1001))
+    rng.standard_normal(16)
+    x2 = rng.standard_normal(16)
+    h = lambda a: hashlib.sha256(a.astype("<f8").tobytes()).hexdigest()
+    assert h(x1) != h(x2)
