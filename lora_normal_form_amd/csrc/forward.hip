@@ -3,8 +3,8 @@
 //
 // Order of steps ("How does Scute plug into vLLM?" and "Where is the
 // cheapest place to compute the remaining slots?", paper-daily.com explainer
-// of "Scute: Exact Batched Serving for PEFT Adapters Beyond LoRA"): the
-// rotation runs in its own pass before the shared GEMM; the base GEMM runs
+// of "Scute: Exact Batched Serving for PEFT Adapters Beyond LoRA"): rows
+// are rotated first, and the rotated rows then share the GEMM; the base GEMM runs
 // once for the whole batch; the own low-rank term is shrunk and expanded per
 // adapter; s multiplies the base output and the low-rank update is added
 // unscaled; the shared VeRA term is computed for every VeRA row of the batch

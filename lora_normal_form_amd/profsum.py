@@ -25,7 +25,16 @@ import sys
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["csrc/decode.hip", "csrc/forward.hip", "csrc/prefill.hip", "csrc/kernels.h"]
+
+
+def kernel_sources():
+    """Every source under csrc/ (kernels and the planners that set their
+    tile order, split factors and launch shapes), sorted."""
+    d = os.path.join(PKG, "csrc")
+    return sorted("csrc/" + f for f in os.listdir(d)
+                  if f.endswith((".hip", ".h", ".cpp")))
+
+
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -58,10 +67,10 @@ def strip_comments(src: str) -> str:
 
 
 def source_sha() -> str:
-    """SHA-256 over the code of the HIP kernel sources (those that exist),
-    comments removed."""
+    """SHA-256 over the code of every source under csrc/ (kernels and their
+    planners), comments removed."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in kernel_sources():
         path = os.path.join(PKG, rel)
         if os.path.exists(path):
             h.update(rel.encode())

@@ -13,10 +13,10 @@ pages' orientation first (``Wf = W.T`` and so on) and then writes every
 formula exactly as the pages do.
 
 Readings taken where the pages leave a step open:
-  * OFT: the pages say only "block-diagonal rotation"; the rotation of each
-    block is the Cayley transform R = (I + Q)(I - Q)^-1 of the adapter's
+  * OFT: the pages name the rotation block-diagonal and nothing more; the
+    rotation of each block is the Cayley transform R = (I + Q)(I - Q)^-1 of the adapter's
     skew-symmetric block Q, applied as x R (row vector).
-  * DoRA: "rescales each column of W + cAB to a learned length m", i.e.
+  * DoRA: every column of W + cAB is brought to its learned length m, i.e.
     W_D = (W + cAB) diag(m / colnorm(W + cAB)), column norms over d_in.
   * VeRA: c = 1; d sits between the shared A and B, e after B.
   * Tokens with adapter id -1 take the base path only.
@@ -30,9 +30,9 @@ import numpy as np
 
 
 # --------------------------------------------------------------------------
-# OFT rotation ("What problem is it solving?": OFT multiplies each layer's
-# input by a block-diagonal rotation matrix; "Where is the cheapest place...":
-# each input row is multiplied by its tenant's block-diagonal matrix)
+# OFT rotation ("What problem is it solving?": an OFT adapter rotates the
+# layer's input; "Where is the cheapest place...": a kernel ahead of the GEMM
+# applies each row's own block-diagonal matrix)
 # --------------------------------------------------------------------------
 
 def cayley(Q: np.ndarray) -> np.ndarray:
@@ -65,8 +65,8 @@ def explicit_rotation(Rblocks: np.ndarray) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# DoRA ("What problem is it solving?": DoRA rescales each output column to a
-# learned length; "Which slots can be merged at load?" and "How does Scute
+# DoRA ("What problem is it solving?": each output column of the adapted
+# weight gets a learned length; "Which slots can be merged at load?" and "How does Scute
 # plug into vLLM?": s = learned length / norm of each column of W + cAB)
 # --------------------------------------------------------------------------
 

@@ -52,11 +52,17 @@ def _config(idx):
     return _cache[idx]
 
 
+# kernels each named workload must run on: 0 generic (fp32), 1 MFMA decode,
+# 2 MFMA prefill; a planner change that sent one of them elsewhere fails here
+NAMED_PATH = {0: 0, 1: 1, 2: 1, 3: 1, 4: 2}
+
+
 @pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
 def test_named_workload_full_size(idx):
     _need_gpu()
     wl, ref = _config(idx)
-    _, y = _run(wl)
+    ld, y = _run(wl)
+    assert ld.batch.info()["path"] == NAMED_PATH[idx], ld.batch.info()
     _assert_parity(wl, y, ref)
 
 
