@@ -196,6 +196,11 @@ scute_status scute_batch_destroy(scute_batch* batch);
  * HIP kernels: OFT rotation, base GEMM with the s / b epilogue, own-term
  * shrink and expand, and the whole-batch shared VeRA term ("How does Scute
  * plug into vLLM?": four steps, the rotation before the GEMM).
+ * Range: inputs must be finite; every intermediate (rotation, shrink
+ * sums, GEMM partials, expand) is held in float32 (the shrink sums and
+ * rotation output are rounded to the activation dtype once as MFMA
+ * operands), so any input scale whose products and sums stay inside the
+ * float32 range is served; there is no fixed-point stage.
  * Errors: SCUTE_E_STATE if the plan is stale or from another layer,
  * SCUTE_E_UNSUPPORTED on a host-only layer, SCUTE_E_INVALID for null or
  * misaligned pointers (16-byte alignment required). */

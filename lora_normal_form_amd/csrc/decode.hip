@@ -811,7 +811,7 @@ k_decode_main(MainArgs a) {
       for (int i = 0; i < 16; ++i)
         Tk[(32 * g + 8 * (i >> 2) + 4 * h + (i & 3)) * 64 + cb * 32 + m] = acc[g][i];
   }
-  wg_barrier();
+  lds_barrier();  // other waves read these LDS writes next
 
   // (b) row pass 1: fold delta W into the rotated rows (delta row r belongs
   //     to sorted row r; delta rows past n_rot are zero) and scale by s
@@ -830,7 +830,7 @@ k_decode_main(MainArgs a) {
     for (int j = 0; j < 2 * MGT; ++j)
       if (j < nj) T4[(rr + 16 * j) * 16 + q4] = (v[j] + dv[j]) * s4[j];
   }
-  wg_barrier();
+  lds_barrier();
 
   // (c) expand: wave w takes row groups w, w + 4, .. of the x rows and both
   //     column blocks. A group's own steps (A rows zero outside each step's
@@ -874,7 +874,7 @@ k_decode_main(MainArgs a) {
     }
   }
   if (a.gv1 > a.gv0) dense_vera<MGT>(a, V, vflag, kc, cb, kp, tid, m, h, ncol);
-  wg_barrier();
+  lds_barrier();
 
   // (d) row pass 2: this slice's tile = T + (V (.) e) + b (b on slice 0 only)
   f32x4 out[2 * MGT];
@@ -930,7 +930,7 @@ k_decode_main(MainArgs a) {
     last_flag = old == a.S - 1;
     if (old == a.S - 1) reset_counter(a.cnt + c);
   }
-  wg_barrier();
+  lds_barrier();  // last_flag is read by every wave
   if (!last_flag) return;
   f32x4 tot[2 * MGT];
 #pragma unroll
@@ -974,7 +974,6 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   // the shrink sums of this forward and the buffer cleared for the next
   float* acc = D.acc32[D.fwd & 1];
   float* acc_next = D.acc32[(D.fwd + 1) & 1];
-  ++D.fwd;
   int nl = 0;
   {
     ProArgs pa{};
@@ -1000,6 +999,8 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
     ++nl;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch k_decode_prologue");
+    // the prologue cleared acc_next: only now may the next forward use it
+    ++D.fwd;
   }
   MainArgs ma{};
   ma.xs = D.xs;

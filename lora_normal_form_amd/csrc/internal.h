@@ -224,11 +224,10 @@ struct PrefillPlan {
   const int32_t* crow = nullptr;          // [n_chunks][128] staged row sources
   const PfProItem* pro_items = nullptr;  // shrinks, rotation
   const DecVeraRow* vrows = nullptr;     // [64 nvb]
-  // per parity: [n][AW] shrink sums in fixed point (int64, units of 2^-32);
-  // forwards alternate between the two and each prologue clears the other
-  long long* acc64[2] = {nullptr, nullptr};
-  uint32_t acc_bytes = 0;
-  mutable uint32_t fwd = 0;
+  // [shrink tiles][K parts][64 x 64] fp32 partial shrink tiles, added in
+  // part order by the last part of a tile to arrive
+  float* tpart = nullptr;
+  uint32_t tpart_bytes = 0;
   uint16_t* tbf = nullptr;    // [n][AW] the finished sums in bf16 (the expand's A operand)
   int32_t* tcnt = nullptr;    // [shrink tiles] arrival counters of the K parts (kept at zero)
   uint32_t tbf_bytes = 0;

@@ -81,6 +81,12 @@ __device__ __forceinline__ void st_sys4(rsrc_t r, uint32_t off, f32x4 v) {
 __device__ __forceinline__ f32x4 ld_sys4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_SYS));
 }
+__device__ __forceinline__ void st_sys1(rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CPOL_SYS);
+}
+__device__ __forceinline__ float ld_sys1(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_SYS));
+}
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ int arrive(int32_t* cnt) {
   return __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);

@@ -228,12 +228,12 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   const size_t o_ones = take(4 * (size_t)d_out);
   const size_t tables = o;
   const size_t o_zeros = take(4 * (size_t)d_out);
-  const size_t acc_bytes = 8 * (size_t)n * P.AW;
-  if (acc_bytes >= ((size_t)1 << 31)) {
+  const size_t tpart_bytes = (size_t)n_tiles * KP * 64 * 64 * 4;
+  if (tpart_bytes >= ((size_t)1 << 31)) {
     P = PrefillPlan{};  // buffer offsets are 32-bit
     return SCUTE_OK;
   }
-  const size_t o_acc0 = take(acc_bytes), o_acc1 = take(acc_bytes);
+  const size_t o_tpart = take(tpart_bytes);
   const size_t tbf_bytes = 2 * (size_t)n * P.AW;
   const size_t o_tbf = take(tbf_bytes), o_tcnt = take(4 * (size_t)n_tiles + 4);
   const size_t part_bytes = (size_t)P.n_split * parts * 32 * 256 * 16;
@@ -282,10 +282,8 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   P.part = (float*)(d + o_part);
   P.cnt = (int32_t*)(d + o_cnt);
   P.part_bytes = (uint32_t)part_bytes;
-  P.acc64[0] = (long long*)(d + o_acc0);
-  P.acc64[1] = (long long*)(d + o_acc1);
-  P.acc_bytes = (uint32_t)acc_bytes;
-  P.fwd = 0;
+  P.tpart = (float*)(d + o_tpart);
+  P.tpart_bytes = (uint32_t)tpart_bytes;
   P.tbf = (uint16_t*)(d + o_tbf);
   P.tcnt = (int32_t*)(d + o_tcnt);
   P.tbf_bytes = (uint32_t)tbf_bytes;

@@ -7,12 +7,11 @@
 //   shrink       t = x A' for 64 rows of a segment x 64 own ranks, and
 //   VeRA shrink  u = (x A_sh) (.) d for 64 VeRA rows x 64 ranks, both over
 //                one K part of 1024 on 32x32x16 bf16 MFMA, operands staged in
-//                LDS by direct loads; the parts add into fixed-point sums
-//                with integer atomics (order-independent, so every forward
-//                gives the same bits), and the last part of a tile to arrive
-//                converts the tile's sums to bf16 for the main kernel; the
-//                fixed-point sums alternate between two buffers and each
-//                prologue clears the one the next forward uses;
+//                LDS by direct loads; each part writes its fp32 partial
+//                tile, and the last part of a tile to arrive adds the parts
+//                in part order (so every forward gives the same bits, at any
+//                input scale fp32 holds) and converts the sums to bf16 for
+//                the main kernel;
 //   rotation     Delta = x (R - I) for 32 rotated rows x 256 columns; R is
 //                block diagonal, so each 32-column MFMA block contracts over
 //                one diagonal block.
@@ -50,18 +49,6 @@
 namespace scute {
 
 namespace {
-
-// Shrink sums are kept in fixed point: int64 in units of 2^-32. Every K
-// slice of a shrink adds its partial sums with integer atomics, which are
-// associative, so the totals do not depend on the order the slices land in
-// (the same bits on every forward). A partial below 2^-9 in magnitude keeps
-// fewer than its 24 bits (absolute error <= 2^-33); values stay far below
-// the 2^31 range.
-constexpr float FX_SCALE = 4294967296.0f;  // 2^32
-__device__ __forceinline__ unsigned long long fx_from(float v) {
-  return (unsigned long long)__float2ll_rn(v * FX_SCALE);
-}
-__device__ __forceinline__ float fx_to(long long v) { return (float)((double)v * 0x1p-32); }
 
 struct PfArgs {
   const uint16_t* x;       // [n][d_in] rows in batch (token) order
@@ -516,12 +503,10 @@ struct PpArgs {
   const DecVeraRow* vrows;      // [64 nvb]
   const uint16_t* A_sh;         // [r_v][d_in]
   uint16_t* dx;                 // [n_rot][d_in] Delta rows by sorted position
-  unsigned long long* acc;      // [n][AW] this forward's shrink sums (zero on entry)
-  unsigned long long* acc_next; // the other buffer, cleared for the next forward
+  float* tpart;                 // [shrink tiles][KP][4 waves][16][64] fp32 partial tiles
   uint16_t* tbf;                // [n][AW] finished sums in bf16
   int32_t* tcnt;                // [shrink tiles] arrival counters
-  uint32_t acc_words;           // n AW
-  uint32_t acc_bytes, tbf_bytes;
+  uint32_t tpart_bytes, tbf_bytes;
   int32_t KP;                   // K parts of a shrink tile
   uint32_t x_bytes, ash_bytes;
   int32_t d_in, AW, RT, r_v;
@@ -624,11 +609,6 @@ __global__ void __launch_bounds__(256) k_prefill_prologue(PpArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 31, h = lane >> 5;
-  {
-    f32x4* z = reinterpret_cast<f32x4*>(a.acc_next);
-    for (uint32_t i = blockIdx.x * 256 + tid; i < a.acc_words / 2; i += gridDim.x * 256)
-      z[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   const PfProItem it = a.items[blockIdx.x];
   const int64_t d_in = a.d_in;
   if (it.type == PP_ROT) {
@@ -689,26 +669,21 @@ __global__ void __launch_bounds__(256) k_prefill_prologue(PpArgs a) {
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   wg_barrier();
   pp_mul(buf1, acc, rb, cb, m, h);
-  // (3) add the partial sums: element i is row 32 rb + 8 (i / 4) + 4 h + i % 4
-  //     of the tile, rank k0 + 32 cb + m
-  const int j = 32 * cb + m;
-  const int col = (vera ? a.RT : 0) + k0 + j;
-  if (j < nk) {
+  const int j = 32 * cb + m;  // rank of this lane's outputs within the tile
+  // (3) store this K part's partial tile (VeRA: scaled by d, which is per
+  //     rank and so commutes with the K sum): element i of wave w, lane l
+  //     at [tile][part][w][i][l], so every store instruction writes 256
+  //     contiguous bytes; written through to memory for the last part
+  const rsrc_t pr = make_rsrc(a.tpart, a.tpart_bytes);
+  const uint32_t tile_off = (uint32_t)(it.pad * a.KP) * 16384u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * rb + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (vera) {
-        if (prow[i] >= 0) atomicAdd(a.acc + (size_t)prow[i] * a.AW + col, fx_from(acc[i] * dsc[i]));
-      } else if (r < it.n) {
-        atomicAdd(a.acc + (size_t)(it.p0 + r) * a.AW + col, fx_from(acc[i]));
-      }
-    }
-  }
-  // (4) the last K part of the tile to arrive converts the tile's sums to
-  //     bf16 (the atomics have completed in memory before each part counts
-  //     its arrival; the sums are read past the caches)
+  for (int i = 0; i < 16; ++i)
+    st_sys1(pr, tile_off + (uint32_t)it.blk * 16384u + (uint32_t)((w * 16 + i) * 64 + lane) * 4u,
+            vera ? acc[i] * dsc[i] : acc[i]);
+  // (4) the last K part of the tile to arrive adds the parts in part order,
+  //     then writes the tile's sums as bf16
   __shared__ int32_t last_part;
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  wait_vm_all();
   lds_barrier();
   if (tid == 0) {
     const int old = arrive(a.tcnt + it.pad);
@@ -718,6 +693,25 @@ __global__ void __launch_bounds__(256) k_prefill_prologue(PpArgs a) {
   lds_barrier();
   if (!last_part) return;
   {
+    float sum[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum[i] = 0.f;
+    for (int p = 0; p < a.KP; ++p) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        v[i] = ld_sys1(pr, tile_off + (uint32_t)p * 16384u + (uint32_t)((w * 16 + i) * 64 + lane) * 4u);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum[i] += v[i];
+    }
+    // transpose through LDS (buf0 is free: every wave is past its last
+    // multiply): T[row][rank], row 32 rb + 8 (i / 4) + 4 h + i % 4, rank j
+    float* T = reinterpret_cast<float*>(buf0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) T[(32 * rb + 8 * (i >> 2) + 4 * h + (i & 3)) * 64 + j] = sum[i];
+  }
+  lds_barrier();
+  {
     // thread -> tile row tid / 4, ranks 16 (tid % 4) .. + 15
     const int r = tid >> 2, c16 = 16 * (tid & 3);
     int32_t row;
@@ -726,21 +720,11 @@ __global__ void __launch_bounds__(256) k_prefill_prologue(PpArgs a) {
     else
       row = r < it.n ? it.p0 + r : -1;
     if (row >= 0 && c16 < nk) {
-      const rsrc_t sr = make_rsrc(a.acc, a.acc_bytes);
-      const int cbase = (vera ? a.RT : 0) + k0 + c16;
-      const uint32_t off = (uint32_t)(((int64_t)row * a.AW + cbase) * 8);
-      f32x4 q[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = ld_sys4(sr, off + 16 * e);
+      const float* T = reinterpret_cast<const float*>(buf0) + r * 64 + c16;
       uint32_t wv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const u32x4 v = __builtin_bit_cast(u32x4, q[e]);
-        const float lo = fx_to((long long)(((unsigned long long)v.y << 32) | v.x));
-        const float hi = fx_to((long long)(((unsigned long long)v.w << 32) | v.z));
-        wv[e] = pack_bf2(__float_as_uint(lo), __float_as_uint(hi));
-      }
-      uint16_t* dst = a.tbf + (size_t)row * a.AW + cbase;
+      for (int e = 0; e < 8; ++e) wv[e] = pack_bf2(__float_as_uint(T[2 * e]), __float_as_uint(T[2 * e + 1]));
+      uint16_t* dst = a.tbf + (size_t)row * a.AW + (vera ? a.RT : 0) + k0 + c16;
       *(GLOBAL u32x4*)dst = u32x4{wv[0], wv[1], wv[2], wv[3]};
       *(GLOBAL u32x4*)(dst + 8) = u32x4{wv[4], wv[5], wv[6], wv[7]};
     }
@@ -753,9 +737,6 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
                             float* y, hipStream_t st, int32_t* launches) {
   const PrefillPlan& P = B->pp;
   // the shrink sums of this forward and the buffer cleared for the next
-  long long* acc = P.acc64[P.fwd & 1];
-  long long* acc_next = P.acc64[(P.fwd + 1) & 1];
-  ++P.fwd;
   int nl = 0;
   if (P.n_pro > 0) {
     PpArgs pa{};
@@ -765,10 +746,8 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
     pa.vrows = P.vrows;
     pa.A_sh = (const uint16_t*)L->A_sh;
     pa.dx = (uint16_t*)B->delta;
-    pa.acc = (unsigned long long*)acc;
-    pa.acc_next = (unsigned long long*)acc_next;
-    pa.acc_words = P.acc_bytes / 8;
-    pa.acc_bytes = P.acc_bytes;
+    pa.tpart = P.tpart;
+    pa.tpart_bytes = P.tpart_bytes;
     pa.tbf = P.tbf;
     pa.tcnt = P.tcnt;
     pa.tbf_bytes = P.tbf_bytes;

@@ -179,3 +179,21 @@ def test_prefill_split_k_parts(parts):
     y = _forward(ld)
     _check(wl, y, ref)
     np.testing.assert_array_equal(_forward(ld), y)
+
+
+@pytest.mark.parametrize("xscale", [2.0 ** -20, 2.0 ** 12])
+def test_prefill_input_scale(xscale):
+    # the shrink sums of the K parts are fp32 partial tiles added in part
+    # order, so the result holds at any input scale fp32 represents: x
+    # scaled by a power of two (exact in bf16), every method, repeat bit for
+    # bit
+    _need_gpu()
+    rng = np.random.default_rng(38)
+    ta = rng.permutation(_segments([200, 150, 130, 170, 90, 60], [0, 1, 3, 4, 9, 10]))
+    wl = _wl("prefill_scale", ta, seed=38, d_out=256)
+    wl.x = wl.x * xscale
+    ld = _load(wl)
+    assert ld.batch.info()["path"] == PREFILL
+    y = _forward(ld)
+    _check(wl, y)
+    np.testing.assert_array_equal(_forward(ld), y)
