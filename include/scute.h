@@ -184,6 +184,22 @@ scute_status scute_unload_adapter(scute_layer* layer, int32_t id, void* stream);
 scute_status scute_plan_batch(scute_layer* layer, const int32_t* token_adapter,
                               int32_t n, void* stream, scute_batch** out);
 
+/* Plan flags for scute_plan_batch_flags. */
+typedef enum scute_plan_flag {
+  /* every forward with the plan gives the same bits for the same inputs:
+   * decode-size batches run the fused MFMA path, whose K slices and shrink
+   * slices are added in a fixed order with no float atomics (the other
+   * paths already add in a fixed order) */
+  SCUTE_PLAN_DETERMINISTIC = 1
+} scute_plan_flag;
+
+/* scute_plan_batch with flags (a bitwise or of scute_plan_flag; 0 gives
+ * scute_plan_batch). Errors as scute_plan_batch, plus SCUTE_E_INVALID for an
+ * unknown flag bit. */
+scute_status scute_plan_batch_flags(scute_layer* layer, const int32_t* token_adapter,
+                                    int32_t n, uint32_t flags, void* stream,
+                                    scute_batch** out);
+
 /* Free a plan (after the streams that used it are synchronised). Null ok.
  * The plan records its device when it is built, so it may be freed before
  * or after its layer. */

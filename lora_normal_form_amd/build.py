@@ -20,8 +20,8 @@ LIB = os.path.join(PKG, "libscute.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-HOST_SRCS = ["layer.cpp", "plan.cpp", "plan_decode.cpp", "plan_prefill.cpp"]
-HIP_SRCS = ["forward.hip", "decode.hip", "prefill.hip"]
+HOST_SRCS = ["layer.cpp", "plan.cpp", "plan_decode.cpp", "plan_prefill.cpp", "plan_fdecode.cpp"]
+HIP_SRCS = ["forward.hip", "decode.hip", "prefill.hip", "fdecode.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include")]

@@ -289,6 +289,7 @@ static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x,
 int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
   (void)L;
   if (B->n == 0) return 0;
+  if (B->fp.enabled) return (B->fp.n_rot_items > 0) + 1;  // rotation + fused main
   if (B->dp.enabled) return 2;  // prologue (gather, rotation, shrinks) + main
   if (B->pp.enabled) return (B->pp.n_pro > 0) + 1;  // prologue (rotation, shrinks) + main
   return (B->n_rot > 0) + (B->max_rank > 0) + (B->n_vera > 0) + 1 +
@@ -297,6 +298,7 @@ int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
 
 scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                             float* y, hipStream_t st, int32_t* launches) {
+  if (B->fp.enabled) return launch_fdecode(L, B, x, W, y, st, launches);
   if (B->dp.enabled) return launch_decode(L, B, x, W, y, st, launches);
   if (B->pp.enabled) return launch_prefill(L, B, x, W, y, st, launches);
   if (L->act == SCUTE_BF16)

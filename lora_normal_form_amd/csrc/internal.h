@@ -166,6 +166,79 @@ struct DecodePlan {
   mutable uint32_t fwd = 0;
 };
 
+// ---- fused decode path (fdecode.hip / plan_fdecode.cpp) --------------------
+// Staged x row of a decode batch (sorted position): the factor vectors of the
+// row's adapter (shared ones / zeros where a slot is absent, so every row runs
+// the same branch-free code), the y row it writes and the x row it stages.
+// 48 bytes.
+enum : int32_t { FR_S = 1, FR_E = 2, FR_B = 4, FR_VERA = 8 };
+struct FdRow {
+  const float* s;  // live s, or ones
+  const float* e;  // VeRA e, or ones
+  const float* b;  // shift b, or zeros
+  const float* d;  // VeRA d, or zeros
+  int32_t tok;     // y row written (-1: padding row)
+  int32_t src;     // x row staged (padding rows repeat a valid token)
+  int32_t flags;   // FR_* of the live slots
+  int32_t rank;    // rank of the row's own term (0: none)
+};
+// One 16-rank step of an own term's expand: ranks [kk, kk + 16) of the
+// term of rank `rank`, for sorted rows [lo, hi) of row group g, against
+// B' = bp. 32 bytes.
+struct FdStep {
+  int32_t kk, rank, lo, hi;
+  const uint16_t* bp;
+  int32_t g, pad;
+};
+// Shrink block: 32 rank rows (rows of adapters' A', or of the shared A_sh)
+// multiplied with the x rows of one row group in the GEMM's K loop. Rank row
+// m's sums go to column col[m] of the shrink buffer for the sorted rows in
+// [lohi[m] & 0xFFFF, lohi[m] >> 16) (own ranks) or for every VeRA row of the
+// group (vera). 768 bytes.
+struct FdXBlock {
+  const uint16_t* arow[32];
+  int32_t col[32];   // -1: unused rank row
+  int32_t lohi[32];
+  int32_t g, vera;
+  int32_t pad[62];
+};
+// Rotation item: rows p0 .. p0 + n - 1 (n <= 4, one adapter; tokens tok[])
+// by the item's columns from c0, P = (R - I)^T blocks of size blk. 48 bytes.
+struct FdRotItem {
+  int32_t p0, n, c0, blk;
+  int32_t tok[4];
+  const uint16_t* P;
+  int64_t pad;
+};
+
+struct FdPlan {
+  bool enabled = false;
+  int32_t MG = 0, g_rot = 0, MGT = 0, M_pad = 0;
+  int32_t S = 1, C = 0, NST = 0;   // K slices, 128-column tiles, 64-k stages per slice
+  int32_t CG = 0;                  // column tiles of the grid (C, or more to carry every shrink block)
+  int32_t RT = 0, AW = 0;          // shrink buffer row: RT own ranks, then r_v VeRA ranks
+  int32_t gv0 = 0, gv1 = 0;        // row groups holding VeRA rows
+  int32_t n_rot_items = 0;
+  int32_t rot_blk = 0;             // block size of every rotation item (8..64), or 0: mixed
+  int32_t rot_cols = 0;            // columns per rotation item (256 for blocks of 64, else 512)
+  int32_t n_xb = 0;                // shrink blocks (block j rides on wave j / CG of tile j % CG)
+  const FdRow* rows = nullptr;     // [M_pad]
+  const FdStep* steps = nullptr;   // own expand steps by row group
+  const int32_t* goff = nullptr;   // [MG + 1]: group g's steps [goff[g], goff[g+1])
+  const int32_t* xoff = nullptr;   // [MG + 1]: group g's shrink blocks [xoff[g], xoff[g+1])
+  const FdXBlock* xb = nullptr;    // [n_xb]
+  const FdRotItem* rot = nullptr;  // [n_rot_items]
+  uint16_t* acc = nullptr;         // [M_pad][AW] finished shrink sums, rounded to bf16
+  float* xpart = nullptr;          // [n_xb][S][4 KB] the slices' partial shrink tiles
+  int32_t* xcnt = nullptr;         // [n_xb] block arrival counters (never reset)
+  uint32_t* xdone = nullptr;       // [n_xb] forward number whose sums the block holds
+  float* part = nullptr;           // [C][S][MG][4][4 KB] split-K partial pieces
+  int32_t* cnt = nullptr;          // [C][MG][4] arrival counters (never reset)
+  int32_t* err = nullptr;          // bounded waits that gave up
+  uint32_t acc_bytes = 0, part_bytes = 0, xpart_bytes = 0;
+  mutable uint32_t fwd = 0;        // forwards launched with this plan
+};
+
 // Chunk of a prefill batch: the rows of one adapter segment (or of rows
 // without an adapter) that one row tile of the prefill GEMM covers: up to 128
 // tokens, or up to 64 tokens followed by their 64 Delta rows when the adapter
@@ -236,6 +309,7 @@ struct PrefillPlan {
 }  // namespace scute
 
 struct scute_batch {
+  uint32_t flags = 0;  // scute_plan_flag bits
   const scute_layer* layer = nullptr;  // compared only: the layer may be destroyed first
   int32_t device = -1;                 // device of the allocations below (-1: none)
   uint64_t epoch = 0;
@@ -263,6 +337,8 @@ struct scute_batch {
   scute::DecodePlan dp;
   void* pf_dev = nullptr;     // prefill-path tables + workspaces (one allocation)
   scute::PrefillPlan pp;
+  void* fd_dev = nullptr;     // fused decode tables + workspaces (one allocation)
+  scute::FdPlan fp;
   int32_t nseg() const { return (int32_t)(seg.size() / 3); }
 };
 
@@ -285,10 +361,20 @@ scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x,
                             int32_t* launches_out);
 int32_t forward_launch_count(const scute_layer* L, const scute_batch* B);
 
+// Decode path selection (environment SCUTE_DECODE, read when a batch is
+// planned): 0 = generic kernels only, 1 = the fused single-kernel path
+// (fdecode.hip), 2 = the two-launch path (decode.hip); unset = DECODE_DEFAULT.
+constexpr int DECODE_DEFAULT = 2;
+
 // decode path (decode.hip / plan.cpp)
 scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t st);
 scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                            float* y, hipStream_t st, int32_t* launches);
+
+// fused decode path (fdecode.hip / plan_fdecode.cpp)
+scute_status build_fdecode_plan(const scute_layer* L, scute_batch* B, hipStream_t st);
+scute_status launch_fdecode(scute_layer* L, const scute_batch* B, const void* x, const void* W,
+                            float* y, hipStream_t st, int32_t* launches);
 
 // prefill path (prefill.hip / plan_prefill.cpp)
 scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_t st);

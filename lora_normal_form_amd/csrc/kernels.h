@@ -84,6 +84,14 @@ __device__ __forceinline__ f32x4 ld_sys4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void st_sys1(rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, CPOL_SYS);
 }
+__device__ __forceinline__ void st_sys2(rsrc_t r, uint32_t off, uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, off, 0, CPOL_SYS);
+}
+__device__ __forceinline__ uint4 ld_sys16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_SYS));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ float ld_sys1(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CPOL_SYS));
 }

@@ -41,18 +41,26 @@ void free_batch_memory(scute_batch* B) {
     if (B->ws) (void)hipFree(B->ws);
     if (B->fast_dev) (void)hipFree(B->fast_dev);
     if (B->pf_dev) (void)hipFree(B->pf_dev);
+    if (B->fd_dev) (void)hipFree(B->fd_dev);
     if (prev != dev && prev >= 0) (void)hipSetDevice(prev);
   }
-  B->dev = B->ws = B->fast_dev = B->pf_dev = nullptr;
+  B->dev = B->ws = B->fast_dev = B->pf_dev = B->fd_dev = nullptr;
 }
 
 }  // namespace
 
 extern "C" scute_status scute_plan_batch(scute_layer* L, const int32_t* token_adapter, int32_t n,
                                          void* stream, scute_batch** out) {
+  return scute_plan_batch_flags(L, token_adapter, n, 0, stream, out);
+}
+
+extern "C" scute_status scute_plan_batch_flags(scute_layer* L, const int32_t* token_adapter, int32_t n,
+                                               uint32_t flags, void* stream, scute_batch** out) {
   try {
     if (!L || !out) return fail(SCUTE_E_INVALID, "scute_plan_batch: null argument");
     *out = nullptr;
+    if (flags & ~(uint32_t)SCUTE_PLAN_DETERMINISTIC)
+      return fail(SCUTE_E_INVALID, "scute_plan_batch_flags: unknown flag bits");
     if (n < 0 || n > (1 << 22)) return fail(SCUTE_E_SHAPE, "scute_plan_batch: n must be in [0, 2^22]");
     if (n > 0 && !token_adapter) return fail(SCUTE_E_INVALID, "scute_plan_batch: token_adapter is null");
     for (int32_t t = 0; t < n; ++t) {
@@ -69,6 +77,7 @@ extern "C" scute_status scute_plan_batch(scute_layer* L, const int32_t* token_ad
     B->device = L->device;
     B->epoch = L->epoch;
     B->n = n;
+    B->flags = flags;
     B->perm.resize(n);
     for (int32_t t = 0; t < n; ++t) B->perm[t] = t;
     auto key = [&](int32_t t) -> int64_t {
@@ -154,8 +163,9 @@ extern "C" scute_status scute_plan_batch(scute_layer* L, const int32_t* token_ad
         delete B;
         return hip_fail(e, "plan upload / workspace");
       }
-      scute_status ds = build_decode_plan(L, B, s);
-      if (ds == SCUTE_OK && !B->dp.enabled) ds = build_prefill_plan(L, B, s);
+      scute_status ds = build_fdecode_plan(L, B, s);
+      if (ds == SCUTE_OK && !B->fp.enabled) ds = build_decode_plan(L, B, s);
+      if (ds == SCUTE_OK && !B->fp.enabled && !B->dp.enabled) ds = build_prefill_plan(L, B, s);
       restore();
       if (ds != SCUTE_OK) {
         free_batch_memory(B);
@@ -186,7 +196,7 @@ extern "C" scute_status scute_batch_info_get(const scute_batch* B, scute_batch_i
   out->n_rot_rows = B->n_rot;
   out->n_vera_rows = B->n_vera;
   out->max_rank = B->max_rank;
-  out->path = B->dp.enabled ? 1 : (B->pp.enabled ? 2 : 0);
+  out->path = (B->fp.enabled || B->dp.enabled) ? 1 : (B->pp.enabled ? 2 : 0);
   return SCUTE_OK;
 }
 

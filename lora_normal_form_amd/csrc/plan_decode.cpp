@@ -42,7 +42,9 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   D = DecodePlan{};
   const int32_t n = B->n;
   const int64_t d_in = L->d_in, d_out = L->d_out;
-  if (env_int("SCUTE_DECODE", 1) == 0) return SCUTE_OK;
+  // the two-launch decode path (gather / rotation / shrink prologue, then
+  // the GEMM): SCUTE_DECODE=2
+  if (env_int("SCUTE_DECODE", DECODE_DEFAULT) != 2 || (B->flags & SCUTE_PLAN_DETERMINISTIC)) return SCUTE_OK;
   if (L->act != SCUTE_BF16 || n <= 0 || n > 256) return SCUTE_OK;
   // K parts of the shrinks: at most 8 of 1024 (own) and 16 of 512 (VeRA)
   if (d_in % 128 != 0 || d_in > 8192 || d_out % 64 != 0) return SCUTE_OK;

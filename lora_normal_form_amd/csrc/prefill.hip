@@ -579,8 +579,8 @@ __device__ void pp_rotate_scalar(const PpArgs& a, const PfProItem& it, int tid) 
 // buffer->LDS loads (one instruction: 2 rows of 512 bytes; 16-byte piece p of
 // row r stored at position p ^ (r & 31), so the 32 rows an MFMA operand read
 // touches fall in distinct banks), two slices in flight in two buffers; wave
-// w multiplies row block w & 1 by rank block w >> 1. One atomic per output
-// and K part.
+// w multiplies row block w & 1 by rank block w >> 1. Each K part stores
+// its fp32 partial tile; the last part to arrive adds them in part order.
 constexpr int PP_ROW = 512;                  // bytes of a staged row (256 k)
 constexpr int PP_BUF = 2 * 64 * PP_ROW;      // 64 x rows, then 64 A rows
 constexpr int PP_LOADS = 16;                 // direct loads per wave and slice

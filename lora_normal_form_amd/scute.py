@@ -79,6 +79,7 @@ SIGNATURES = {
     "scute_load_adapter": (C.c_int32, [_P, C.c_int32, C.POINTER(AdapterDesc), _P, _P]),
     "scute_unload_adapter": (C.c_int32, [_P, C.c_int32, _P]),
     "scute_plan_batch": (C.c_int32, [_P, _P, C.c_int32, _P, C.POINTER(_P)]),
+    "scute_plan_batch_flags": (C.c_int32, [_P, _P, C.c_int32, C.c_uint32, _P, C.POINTER(_P)]),
     "scute_batch_destroy": (C.c_int32, [_P]),
     "scute_layer_forward": (C.c_int32, [_P, _P, _P, _P, _P, _P]),
     "scute_cost_model": (C.c_int32, [_P, _P, C.POINTER(Cost)]),
@@ -174,11 +175,22 @@ def scute_unload_adapter(layer: int, id: int, stream=None) -> None:
     _check(lib.scute_unload_adapter(layer, id, _stream_ptr(stream)))
 
 
+PLAN_DETERMINISTIC = 1
+
+
 def scute_plan_batch(layer: int, token_adapter, stream=None) -> int:
     ta = np.ascontiguousarray(np.asarray(token_adapter, dtype=np.int32))
     h = _P()
     _check(lib.scute_plan_batch(layer, ta.ctypes.data if ta.size else None, int(ta.size),
                                 _stream_ptr(stream), C.byref(h)))
+    return h.value
+
+
+def scute_plan_batch_flags(layer: int, token_adapter, flags: int, stream=None) -> int:
+    ta = np.ascontiguousarray(np.asarray(token_adapter, dtype=np.int32))
+    h = _P()
+    _check(lib.scute_plan_batch_flags(layer, ta.ctypes.data if ta.size else None, int(ta.size),
+                                      int(flags), _stream_ptr(stream), C.byref(h)))
     return h.value
 
 
@@ -313,7 +325,9 @@ class Layer:
     def unload(self, id, stream=None):
         scute_unload_adapter(self.h, id, stream)
 
-    def plan(self, token_adapter, stream=None) -> "Batch":
+    def plan(self, token_adapter, stream=None, deterministic=False) -> "Batch":
+        if deterministic:
+            return Batch(self, scute_plan_batch_flags(self.h, token_adapter, PLAN_DETERMINISTIC, stream))
         return Batch(self, scute_plan_batch(self.h, token_adapter, stream))
 
     def forward(self, batch, x, W, y, stream=None):

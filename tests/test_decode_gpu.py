@@ -1,6 +1,7 @@
-"""GPU parity of the MFMA decode path (bf16, up to 256 rows, d_in % 256 and
-d_out % 128 aligned) against the fp64 oracle, plus agreement with the generic
-kernels on the same inputs.
+"""GPU parity of the MFMA decode paths (bf16, up to 256 rows) against the
+fp64 oracle, plus agreement with the generic kernels on the same inputs. Every
+test runs on both decode paths: the fused single-kernel one (SCUTE_DECODE=1)
+and the two-launch one (SCUTE_DECODE=2).
 
 Bars as in test_parity_gpu: max|y - ref| <= 1e-2 max|ref| and every touched
 adapter's mean effect error <= 1% of its effect.
@@ -39,6 +40,12 @@ class _env:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
+
+
+@pytest.fixture(autouse=True, params=[1, 2], ids=["fused", "two_launch"])
+def decode_mode(request):
+    with _env(SCUTE_DECODE=request.param):
+        yield request.param
 
 
 def _forward(wl, expect_path=None, **env):
@@ -89,15 +96,16 @@ def _wl(n, seed, d_in=512, d_out=384, vera_rank=64, none_frac=0.1, adapters=MIX,
 
 
 @pytest.mark.parametrize("n", [1, 5, 33, 77, 128, 200, 256])
-def test_decode_path_mixed(n):
-    # the MFMA path stages ceil(n / 32) row groups plus one per 32 rotated
-    # rows, at most 9; larger batches run the generic kernels
+def test_decode_path_mixed(n, decode_mode):
+    # the MFMA paths stage ceil(n / 32) row groups plus one per 32 rotated
+    # rows, at most 8 (fused) or 9 (two-launch); larger batches run the
+    # generic kernels
     _need_gpu()
     wl = _wl(n, seed=n)
     ld, y = _forward(wl)
     info = ld.batch.info()
     groups = -(-n // 32) + -(-info["n_rot_rows"] // 32)
-    assert info["path"] == (1 if groups <= 9 else 0), info
+    assert info["path"] == (1 if groups <= (8 if decode_mode == 1 else 9) else 0), info
     _check(wl, y)
 
 
@@ -115,7 +123,7 @@ def test_decode_long_k_slices_with_w_through_lds(splitk):
     # staged row groups, where W passes through each wave's LDS block
     _need_gpu()
     wl = _wl(100, seed=61, d_in=4096, d_out=1024)
-    ld, y = _forward(wl, expect_path=1, SCUTE_DECODE_SPLITK=splitk)
+    ld, y = _forward(wl, expect_path=1, SCUTE_DECODE_SPLITK=splitk, SCUTE_FD_SPLITK=splitk)
     info = ld.batch.info()
     assert -(-wl.n // 32) + -(-info["n_rot_rows"] // 32) <= 5, info
     _check(wl, y)
@@ -123,10 +131,10 @@ def test_decode_long_k_slices_with_w_through_lds(splitk):
 
 @pytest.mark.parametrize("splitk", [1, 2, 4])
 def test_decode_path_split_k(splitk):
-    # S = 1 stores y directly; S > 1 adds partial products with atomics
+    # S = 1 stores y directly; S > 1 combines the slices' partial products
     _need_gpu()
     wl = _wl(96, seed=11, d_in=1024)
-    _, y = _forward(wl, expect_path=1, SCUTE_DECODE_SPLITK=splitk)
+    _, y = _forward(wl, expect_path=1, SCUTE_DECODE_SPLITK=splitk, SCUTE_FD_SPLITK=splitk)
     _check(wl, y)
 
 
@@ -216,3 +224,31 @@ def test_decode_many_expand_steps_per_row_group(d_out):
                                     vera_rank=256, assign="explicit", token_adapter=ta, seed=51))
     _, y = _forward(wl, expect_path=1)
     _check(wl, y)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_deterministic_plan_is_bit_repeatable(idx, decode_mode):
+    # a plan built with SCUTE_PLAN_DETERMINISTIC runs the fused decode path
+    # (K slices and shrink slices added in a fixed order, no float atomics),
+    # whatever path the environment prefers, and gives the same bits on
+    # every forward, also after other work ran on the device in between
+    _need_gpu()
+    from lora_normal_form_amd import workload as glue
+    from synth import make_config
+    wl = make_config(idx)
+    print(f"\n[gpu] deterministic {wl.name}", flush=True)
+    ld = glue.load(wl, device=0, deterministic=True)
+    assert ld.batch.info()["path"] == 1, ld.batch.info()
+    outs = []
+    for i in range(4):
+        ld.y.fill_(float("nan"))
+        ld.layer.forward(ld.batch, ld.x, ld.W, ld.y)
+        torch.cuda.synchronize()
+        outs.append(ld.y.cpu().numpy().copy())
+        if i == 1:
+            other = glue.load(_wl(64, seed=99), device=0)
+            other.layer.forward(other.batch, other.x, other.W, other.y)
+            torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
+    _check(wl, outs[0].astype(np.float64))

@@ -7,6 +7,8 @@ The five named workloads run at full size and are compared element by
 element (the oracle finishes each in seconds).
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -63,6 +65,27 @@ def test_named_workload_full_size(idx):
     wl, ref = _config(idx)
     ld, y = _run(wl)
     assert ld.batch.info()["path"] == NAMED_PATH[idx], ld.batch.info()
+    _assert_parity(wl, y, ref)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+@pytest.mark.parametrize("mode", [1, 2], ids=["fused", "two_launch"])
+def test_named_decode_workload_each_path(idx, mode):
+    # the decode workloads on each MFMA decode path by name (SCUTE_DECODE)
+    _need_gpu()
+    from lora_normal_form_amd import workload as glue
+    wl, ref = _config(idx)
+    old = os.environ.get("SCUTE_DECODE")
+    os.environ["SCUTE_DECODE"] = str(mode)
+    try:
+        ld = glue.load(wl, device=0)
+    finally:
+        if old is None:
+            del os.environ["SCUTE_DECODE"]
+        else:
+            os.environ["SCUTE_DECODE"] = old
+    ld, y = _run(wl, ld)
+    assert ld.batch.info()["path"] == 1, ld.batch.info()
     _assert_parity(wl, y, ref)
 
 
