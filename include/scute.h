@@ -224,6 +224,32 @@ scute_status scute_layer_forward(scute_layer* layer, const scute_batch* batch,
                                  const void* x, const void* W, float* y,
                                  void* stream);
 
+/* Bytes of the static device scratch that scute_layer_forward_noalloc uses
+ * (one copy per device, held until the process ends). */
+#define SCUTE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* The forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * it needs no plan and allocates nothing. token_adapter is a DEVICE int32
+ * array [n] (-1: base path only); x, W and y are as in scute_layer_forward.
+ * The batch runs in token order on the generic kernels (the same arithmetic
+ * as scute_layer_forward's generic path); the rotation output and shrink
+ * sums live in the library's static scratch of SCUTE_NOALLOC_SCRATCH_BYTES
+ * on the layer's device, which holds n * d_in * dtype_size (only when a
+ * loaded adapter rotates) + n * max loaded rank * 4 + n * r_v * 4 (only when
+ * a VeRA adapter is loaded) bytes, each part rounded up to 256. Every call on
+ * a device shares that scratch and overwrites what it reads, so calls that
+ * overlap on one device race: order them on one stream. Ids are checked on
+ * the device: a row whose id is out of range or not loaded gets NaN.
+ * Errors: SCUTE_E_SHAPE if n is outside [0, 65535] or the batch needs more
+ * scratch than there is; SCUTE_E_INVALID for null or misaligned pointers
+ * (16-byte x, W, y; 4-byte token_adapter); SCUTE_E_STATE if a VeRA adapter
+ * is loaded and the shared pair is not set; SCUTE_E_UNSUPPORTED on a
+ * host-only layer or a device index past 63. */
+scute_status scute_layer_forward_noalloc(scute_layer* layer, const int32_t* token_adapter,
+                                         int32_t n, const void* x, const void* W, float* y,
+                                         void* stream);
+
 /* Algorithmic bytes / FLOPs / launches of one forward with this plan. */
 scute_status scute_cost_model(const scute_layer* layer, const scute_batch* batch,
                               scute_cost* out);

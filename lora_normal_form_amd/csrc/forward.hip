@@ -20,6 +20,8 @@
 
 #include <string.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace scute {
@@ -35,24 +37,42 @@ __device__ __forceinline__ void stf(uint16_t* p, size_t i, float v) {
   p[i] = (uint16_t)(u >> 16);
 }
 
+// Row p's x row: perm[p] in a planned batch, p itself when the batch is
+// taken in token order (perm null).
+__device__ __forceinline__ int32_t src_row(const int32_t* perm, int32_t p) { return perm ? perm[p] : p; }
+// Row p's adapter: its id, -1 (base path only), or -2 for an id that is out
+// of range or not loaded (ids of a planned batch are checked on the host, so
+// only a batch taken in token order from device memory can hold one).
+__device__ __forceinline__ int32_t row_id(const int32_t* ra, int32_t p, const SlotEntry* table, int32_t na) {
+  const int32_t a = ra[p];
+  if (a == -1) return -1;
+  if (a < 0 || a >= na || !(table[a].flags & F_LOADED)) return -2;
+  return a;
+}
+
 // ---------------------------------------------------------------------------
 // rotation: delta[p][col] = sum_i x[perm[p]][kb*blk + i] * P[kb][i][col - kb*blk],
-// P stored transposed per block
-// grid (ceil(d_in / 256), n_rot)
+// P stored transposed per block; rows without a rotation get zero
+// grid (ceil(d_in / 256), rows)
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k_rotate_ref(const T* __restrict__ x,
                                                     const int32_t* __restrict__ perm,
                                                     const int32_t* __restrict__ row_adapter,
-                                                    const SlotEntry* __restrict__ table,
+                                                    const SlotEntry* __restrict__ table, int32_t na,
                                                     int64_t d_in, T* __restrict__ delta) {
   const int32_t p = blockIdx.y;
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (col >= d_in) return;
-  const SlotEntry E = table[row_adapter[p]];
+  const int32_t a = row_id(row_adapter, p, table, na);
+  if (a < 0 || !(table[a].flags & F_R)) {
+    stf(delta, (size_t)p * d_in + col, 0.f);
+    return;
+  }
+  const SlotEntry E = table[a];
   const int32_t blk = E.blk;
   const int64_t kb = col / blk, jj = col - kb * blk;
-  const T* xr = x + (size_t)perm[p] * d_in + kb * blk;
+  const T* xr = x + (size_t)src_row(perm, p) * d_in + kb * blk;
   const T* Pt = (const T*)E.P + ((size_t)kb * blk + jj) * blk;  // (R - I)^T row jj
   float acc = 0.f;
   for (int32_t i = 0; i < blk; ++i) acc += ldf(xr, i) * ldf(Pt, i);
@@ -78,12 +98,12 @@ template <typename T>
 __global__ void __launch_bounds__(256) k_shrink_ref(const T* __restrict__ x,
                                                     const int32_t* __restrict__ perm,
                                                     const int32_t* __restrict__ row_adapter,
-                                                    const SlotEntry* __restrict__ table,
+                                                    const SlotEntry* __restrict__ table, int32_t na,
                                                     int64_t d_in, int32_t max_rank,
                                                     float* __restrict__ t) {
   __shared__ float red[4];
   const int32_t p = blockIdx.y, k = blockIdx.x;
-  const int32_t a = row_adapter[p];
+  const int32_t a = row_id(row_adapter, p, table, na);
   bool live = false;
   SlotEntry E{};
   if (a >= 0) {
@@ -94,7 +114,7 @@ __global__ void __launch_bounds__(256) k_shrink_ref(const T* __restrict__ x,
     if (threadIdx.x == 0) t[(size_t)p * max_rank + k] = 0.f;
     return;
   }
-  const T* xr = x + (size_t)perm[p] * d_in;
+  const T* xr = x + (size_t)src_row(perm, p) * d_in;
   const T* Ar = (const T*)E.A + (size_t)k * d_in;
   float acc = 0.f;
   for (int64_t i = threadIdx.x; i < d_in; i += 256) acc += ldf(xr, i) * ldf(Ar, i);
@@ -104,21 +124,24 @@ __global__ void __launch_bounds__(256) k_shrink_ref(const T* __restrict__ x,
 
 // ---------------------------------------------------------------------------
 // VeRA shrink over the whole batch: u[p][k] = d_a[k] * (x[perm[p]] . A_sh[k])
-// for every VeRA row p = vera_pos[v]; grid (r_v, n_vera)
+// for every VeRA row p = vera_pos[v]; grid (r_v, n_vera); with vera_pos
+// null, grid (r_v, rows) and rows without a VeRA term are skipped
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k_vera_shrink_ref(const T* __restrict__ x,
                                                          const int32_t* __restrict__ perm,
                                                          const int32_t* __restrict__ row_adapter,
                                                          const int32_t* __restrict__ vera_pos,
-                                                         const SlotEntry* __restrict__ table,
+                                                         const SlotEntry* __restrict__ table, int32_t na,
                                                          const T* __restrict__ A_sh, int64_t d_in,
                                                          int32_t r_v, float* __restrict__ u) {
   __shared__ float red[4];
   const int32_t k = blockIdx.x;
-  const int32_t p = vera_pos[blockIdx.y];
-  const SlotEntry E = table[row_adapter[p]];
-  const T* xr = x + (size_t)perm[p] * d_in;
+  const int32_t p = vera_pos ? vera_pos[blockIdx.y] : (int32_t)blockIdx.y;
+  const int32_t a = row_id(row_adapter, p, table, na);
+  if (a < 0 || !(table[a].flags & F_VERA)) return;  // uniform over the block
+  const SlotEntry E = table[a];
+  const T* xr = x + (size_t)src_row(perm, p) * d_in;
   const T* Ar = A_sh + (size_t)k * d_in;
   float acc = 0.f;
   for (int64_t i = threadIdx.x; i < d_in; i += 256) acc += ldf(xr, i) * ldf(Ar, i);
@@ -129,15 +152,16 @@ __global__ void __launch_bounds__(256) k_vera_shrink_ref(const T* __restrict__ x
 // ---------------------------------------------------------------------------
 // base GEMM with epilogue, 32x32 output tile per block, LDS-staged operands:
 //   y[perm[p]][j] = (x[perm[p]] . W[j] + [p < n_rot] delta[p] . W[j]) * s[j] + b[j]
-// grid (ceil(d_out/32), ceil(n/32)), 256 threads, 4 outputs per thread
+// grid (ceil(d_out/32), ceil(n/32)), 256 threads, 4 outputs per thread; a
+// row with an unusable adapter id gets NaN
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const T* __restrict__ W,
                                                   const T* __restrict__ delta,
                                                   const int32_t* __restrict__ perm,
                                                   const int32_t* __restrict__ row_adapter,
-                                                  const SlotEntry* __restrict__ table, int32_t n,
-                                                  int32_t n_rot, int64_t d_in, int64_t d_out,
+                                                  const SlotEntry* __restrict__ table, int32_t na,
+                                                  int32_t n, int32_t n_rot, int64_t d_in, int64_t d_out,
                                                   float* __restrict__ y) {
   // 128 k per round: every thread's 32 loads of a round are in flight
   // together, so a round costs one memory round trip
@@ -158,7 +182,7 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
         const int32_t p = p0 + r;
         const int64_t j = j0 + r;
         const bool xrow = pass == 0 ? p < n : p < n_rot;
-        const T* xsrc = pass == 0 ? (p < n ? x + (size_t)perm[p] * d_in : x)
+        const T* xsrc = pass == 0 ? (p < n ? x + (size_t)src_row(perm, p) * d_in : x)
                                   : delta + (size_t)min(p, max(n_rot - 1, 0)) * d_in;
 #pragma unroll
         for (int cq = 0; cq < KR / 32; ++cq) {
@@ -191,13 +215,15 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
     const int32_t p = p0 + ty + 8 * q;
     if (p >= n) continue;
     float v = acc[q];
-    const int32_t a = row_adapter[p];
+    const int32_t a = row_id(row_adapter, p, table, na);
     if (a >= 0) {
       const SlotEntry E = table[a];
       if (E.flags & F_S) v *= E.s[j];
       if (E.flags & F_B) v += E.b[j];
+    } else if (a == -2) {
+      v = __builtin_nanf("");
     }
-    y[(size_t)perm[p] * d_out + j] = v;
+    y[(size_t)src_row(perm, p) * d_out + j] = v;
   }
 }
 
@@ -211,13 +237,13 @@ __global__ void __launch_bounds__(256) k_expand_ref(const float* __restrict__ t,
                                                     const T* __restrict__ B_sh,
                                                     const int32_t* __restrict__ perm,
                                                     const int32_t* __restrict__ row_adapter,
-                                                    const SlotEntry* __restrict__ table,
+                                                    const SlotEntry* __restrict__ table, int32_t na,
                                                     int32_t max_rank, int32_t r_v, int64_t d_out,
                                                     float* __restrict__ y) {
   const int32_t p = blockIdx.y;
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (j >= d_out) return;
-  const int32_t a = row_adapter[p];
+  const int32_t a = row_id(row_adapter, p, table, na);
   if (a < 0) return;
   const SlotEntry E = table[a];
   float v = 0.f;
@@ -233,7 +259,7 @@ __global__ void __launch_bounds__(256) k_expand_ref(const float* __restrict__ t,
     for (int32_t k = 0; k < r_v; ++k) w += up[k] * ldf(Bj, k);
     v += E.ve[j] * w;
   }
-  if (E.flags & (F_TERM | F_VERA)) y[(size_t)perm[p] * d_out + j] += v;
+  if (E.flags & (F_TERM | F_VERA)) y[(size_t)src_row(perm, p) * d_out + j] += v;
 }
 
 // ---------------------------------------------------------------------------
@@ -251,34 +277,34 @@ static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x,
   if (B->n_rot > 0) {
     ProfScope ps(L, st, "rotate");
     hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), B->n_rot), dim3(256), 0, st, x,
-                       B->d_perm, B->d_row_adapter, L->table_dev, d_in, (T*)B->delta);
+                       B->d_perm, B->d_row_adapter, L->table_dev, L->max_adapters, d_in, (T*)B->delta);
     ++nl;
   }
   if (B->max_rank > 0) {
     ProfScope ps(L, st, "shrink");
     hipLaunchKernelGGL(k_shrink_ref<T>, dim3(B->max_rank, n), dim3(256), 0, st, x, B->d_perm,
-                       B->d_row_adapter, L->table_dev, d_in, B->max_rank, B->t);
+                       B->d_row_adapter, L->table_dev, L->max_adapters, d_in, B->max_rank, B->t);
     ++nl;
   }
   if (B->n_vera > 0) {
     ProfScope ps(L, st, "vera_shrink");
     hipLaunchKernelGGL(k_vera_shrink_ref<T>, dim3(L->r_v, B->n_vera), dim3(256), 0, st, x,
-                       B->d_perm, B->d_row_adapter, B->d_vera_pos, L->table_dev,
+                       B->d_perm, B->d_row_adapter, B->d_vera_pos, L->table_dev, L->max_adapters,
                        (const T*)L->A_sh, d_in, L->r_v, B->u);
     ++nl;
   }
   {
     ProfScope ps(L, st, "gemm");
     hipLaunchKernelGGL(k_gemm_ref<T>, dim3(cdiv(d_out, 32), cdiv(n, 32)), dim3(256), 0, st, x, W,
-                       (const T*)B->delta, B->d_perm, B->d_row_adapter, L->table_dev, n,
-                       B->n_rot, d_in, d_out, y);
+                       (const T*)B->delta, B->d_perm, B->d_row_adapter, L->table_dev, L->max_adapters,
+                       n, B->n_rot, d_in, d_out, y);
     ++nl;
   }
   if (B->max_rank > 0 || B->n_vera > 0) {
     ProfScope ps(L, st, "expand");
     hipLaunchKernelGGL(k_expand_ref<T>, dim3(cdiv(d_out, 256), n), dim3(256), 0, st, B->t, B->u,
-                       (const T*)L->B_sh, B->d_perm, B->d_row_adapter, L->table_dev, B->max_rank,
-                       L->r_v, d_out, y);
+                       (const T*)L->B_sh, B->d_perm, B->d_row_adapter, L->table_dev, L->max_adapters,
+                       B->max_rank, L->r_v, d_out, y);
     ++nl;
   }
   SCUTE_HIP_CHECK(hipGetLastError());
@@ -367,4 +393,134 @@ extern "C" scute_status scute_profile_read(scute_layer* L, scute_kernel_time* ou
     L->prof_count[i] = 0;
   }
   return SCUTE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// forward without allocation: the generic kernels on the batch in token
+// order, their rotation output and shrink sums in a static device array
+// ---------------------------------------------------------------------------
+namespace scute {
+namespace {
+
+// Each device that loads this library holds its own copy until the process
+// ends. Host code reaches it only through the address hipGetSymbolAddress
+// returns on that device (the name is a host-side stand-in there).
+static __device__ __align__(256) uint8_t scratch[SCUTE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[NOALLOC_MAX_DEVICES] = {};
+
+// the layer-wide facts the token-order forward needs (recomputed after
+// every load / unload)
+void layer_facts(scute_layer* L) {
+  if (L->na_epoch == L->epoch) return;
+  int32_t rk = 0;
+  bool rot = false;
+  for (const SlotEntry& E : L->table) {
+    if (!(E.flags & F_LOADED)) continue;
+    if ((E.flags & F_TERM) && E.rank > rk) rk = E.rank;
+    if (E.flags & F_R) rot = true;
+  }
+  L->na_max_rank = rk;
+  L->na_rot = rot;
+  L->na_epoch = L->epoch;
+}
+
+template <typename T>
+void launch_noalloc(scute_layer* L, const int32_t* ta, int32_t n, const T* x, const T* W, float* y,
+                    uint8_t* ws, size_t o_t, size_t o_u, hipStream_t st) {
+  const int64_t d_in = L->d_in, d_out = L->d_out;
+  const int32_t na = L->max_adapters, rk = L->na_max_rank;
+  const bool vera = L->n_vera_loaded > 0;
+  T* delta = (T*)ws;
+  float* t = (float*)(ws + o_t);
+  float* u = (float*)(ws + o_u);
+  if (L->na_rot)
+    hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), n), dim3(256), 0, st, x, nullptr, ta,
+                       L->table_dev, na, d_in, delta);
+  if (rk > 0)
+    hipLaunchKernelGGL(k_shrink_ref<T>, dim3(rk, n), dim3(256), 0, st, x, nullptr, ta, L->table_dev, na,
+                       d_in, rk, t);
+  if (vera)
+    hipLaunchKernelGGL(k_vera_shrink_ref<T>, dim3(L->r_v, n), dim3(256), 0, st, x, nullptr, ta, nullptr,
+                       L->table_dev, na, (const T*)L->A_sh, d_in, L->r_v, u);
+  hipLaunchKernelGGL(k_gemm_ref<T>, dim3(cdiv(d_out, 32), cdiv(n, 32)), dim3(256), 0, st, x, W,
+                     (const T*)delta, nullptr, ta, L->table_dev, na, n, L->na_rot ? n : 0, d_in, d_out, y);
+  if (rk > 0 || vera)
+    hipLaunchKernelGGL(k_expand_ref<T>, dim3(cdiv(d_out, 256), n), dim3(256), 0, st, t, u,
+                       (const T*)L->B_sh, nullptr, ta, L->table_dev, na, rk, L->r_v, d_out, y);
+}
+
+}  // namespace
+
+// Takes the device address of `scratch` on `device` (which must be
+// current), once per device.
+scute_status noalloc_setup(int32_t device) {
+  if (device < 0 || device >= NOALLOC_MAX_DEVICES) return SCUTE_OK;  // the forward reports it
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (g_scratch[device]) return SCUTE_OK;
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+  g_scratch[device] = p;
+  return SCUTE_OK;
+}
+
+}  // namespace scute
+
+extern "C" scute_status scute_layer_forward_noalloc(scute_layer* L, const int32_t* token_adapter, int32_t n,
+                                                    const void* x, const void* W, float* y, void* stream) {
+  using namespace scute;
+  try {
+    if (!L) return fail(SCUTE_E_INVALID, "scute_layer_forward_noalloc: layer is null");
+    if (L->device < 0)
+      return fail(SCUTE_E_UNSUPPORTED, "scute_layer_forward_noalloc: host-only layer has no forward");
+    if (n < 0 || n > 65535) return fail(SCUTE_E_SHAPE, "scute_layer_forward_noalloc: n must be in [0, 65535]");
+    if (n == 0) return SCUTE_OK;
+    if (!token_adapter || !x || !W || !y)
+      return fail(SCUTE_E_INVALID, "scute_layer_forward_noalloc: null token_adapter, x, W or y");
+    if ((((uintptr_t)x | (uintptr_t)W | (uintptr_t)y) & 15) || ((uintptr_t)token_adapter & 3))
+      return fail(SCUTE_E_INVALID,
+                  "scute_layer_forward_noalloc: x, W, y must be 16-byte and token_adapter 4-byte aligned");
+    const bool vera = L->n_vera_loaded > 0;
+    if (vera && (!L->A_sh || !L->B_sh))
+      return fail(SCUTE_E_STATE, "scute_layer_forward_noalloc: shared VeRA pair not set");
+    layer_facts(L);
+    auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    const size_t es = dtype_size(L->act);
+    const size_t o_t = L->na_rot ? al((size_t)n * L->d_in * es) : 0;
+    const size_t o_u = o_t + al((size_t)n * L->na_max_rank * 4);
+    const size_t need = o_u + (vera ? (size_t)n * L->r_v * 4 : 0);
+    if (need > (size_t)SCUTE_NOALLOC_SCRATCH_BYTES)
+      return fail(SCUTE_E_SHAPE, "scute_layer_forward_noalloc: the batch needs " + std::to_string(need) +
+                                     " bytes of scratch, more than the " +
+                                     std::to_string((size_t)SCUTE_NOALLOC_SCRATCH_BYTES) + " it has");
+    if (L->device >= NOALLOC_MAX_DEVICES)
+      return fail(SCUTE_E_UNSUPPORTED, "scute_layer_forward_noalloc: device index past 63");
+    int prev = -1;
+    (void)hipGetDevice(&prev);
+    if (prev != L->device) (void)hipSetDevice(L->device);
+    scute_status stt = noalloc_setup(L->device);
+    void* ws = nullptr;
+    {
+      std::lock_guard<std::mutex> g(g_scratch_mu);
+      ws = g_scratch[L->device];
+    }
+    if (stt == SCUTE_OK) {
+      hipStream_t st = (hipStream_t)stream;
+      if (L->act == SCUTE_BF16)
+        launch_noalloc<uint16_t>(L, token_adapter, n, (const uint16_t*)x, (const uint16_t*)W, y,
+                                 (uint8_t*)ws, o_t, o_u, st);
+      else
+        launch_noalloc<float>(L, token_adapter, n, (const float*)x, (const float*)W, y, (uint8_t*)ws, o_t,
+                              o_u, st);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) stt = hip_fail(e, "scute_layer_forward_noalloc: launch");
+    }
+    if (prev != L->device && prev >= 0) (void)hipSetDevice(prev);
+    return stt;
+  } catch (...) {
+    return fail(SCUTE_E_INVALID, "scute_layer_forward_noalloc: unexpected error");
+  }
 }

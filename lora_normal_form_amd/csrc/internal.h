@@ -67,6 +67,10 @@ struct scute_layer {
   int32_t n_vera_loaded = 0;
   uint64_t epoch = 1;  // bumps on every load / unload
   int32_t num_cu = 0;
+  // facts of the loaded adapters for the token-order forward, as of na_epoch
+  uint64_t na_epoch = 0;
+  int32_t na_max_rank = 0;
+  bool na_rot = false;
   // kernel timing (scute_profile_enable)
   bool profiling = false;
   std::vector<scute::ProfEvent> prof_pending;
@@ -354,6 +358,10 @@ scute_status hip_fail(hipError_t e, const char* what);
   } while (0)
 
 size_t dtype_size(int32_t dt);
+
+// no-allocation forward (forward.hip): takes the device address of its
+// static scratch on `device` (current), once per device
+scute_status noalloc_setup(int32_t device);
 
 // forward launcher (forward.hip)
 scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x,

@@ -258,6 +258,13 @@ extern "C" scute_status scute_layer_create(int32_t device, int64_t d_in, int64_t
         delete L;
         return hip_fail(e, "hipMemset(slot table)");
       }
+      // the no-allocation forward's scratch address on this device
+      scute_status ns = noalloc_setup(device);
+      if (ns != SCUTE_OK) {
+        (void)hipFree(L->table_dev);
+        delete L;
+        return ns;
+      }
     }
     *out = L;
     return SCUTE_OK;

@@ -82,6 +82,7 @@ SIGNATURES = {
     "scute_plan_batch_flags": (C.c_int32, [_P, _P, C.c_int32, C.c_uint32, _P, C.POINTER(_P)]),
     "scute_batch_destroy": (C.c_int32, [_P]),
     "scute_layer_forward": (C.c_int32, [_P, _P, _P, _P, _P, _P]),
+    "scute_layer_forward_noalloc": (C.c_int32, [_P, _P, C.c_int32, _P, _P, _P, _P]),
     "scute_cost_model": (C.c_int32, [_P, _P, C.POINTER(Cost)]),
     "scute_adapter_info_get": (C.c_int32, [_P, C.c_int32, C.POINTER(AdapterInfo)]),
     "scute_read_slot": (C.c_int32, [_P, C.c_int32, C.c_int32, _P, C.c_int64]),
@@ -200,6 +201,12 @@ def scute_batch_destroy(batch: int) -> None:
 
 def scute_layer_forward(layer: int, batch: int, x, W, y, stream=None) -> None:
     _check(lib.scute_layer_forward(layer, batch, _ptr(x), _ptr(W), _ptr(y), _stream_ptr(stream)))
+
+
+def scute_layer_forward_noalloc(layer: int, token_adapter, n: int, x, W, y, stream=None) -> None:
+    """token_adapter: a device int32 tensor [n] (the ids stay on the device)."""
+    _check(lib.scute_layer_forward_noalloc(layer, _ptr(token_adapter), int(n), _ptr(x), _ptr(W), _ptr(y),
+                                           _stream_ptr(stream)))
 
 
 def scute_cost_model(layer: int, batch: int) -> Dict:
@@ -332,6 +339,10 @@ class Layer:
 
     def forward(self, batch, x, W, y, stream=None):
         scute_layer_forward(self.h, batch.h, x, W, y, stream)
+        return y
+
+    def forward_noalloc(self, token_adapter, x, W, y, stream=None):
+        scute_layer_forward_noalloc(self.h, token_adapter, token_adapter.shape[0], x, W, y, stream)
         return y
 
     def cost(self, batch):
