@@ -190,12 +190,31 @@ typedef enum scute_plan_flag {
    * decode-size batches run the fused MFMA path, whose K slices and shrink
    * slices are added in a fixed order with no float atomics (the other
    * paths already add in a fixed order) */
-  SCUTE_PLAN_DETERMINISTIC = 1
+  SCUTE_PLAN_DETERMINISTIC = 1,
+  /* Route variants of the two-launch decode path, for the route comparison
+   * and time model of "Where is the cheapest place to compute the remaining
+   * slots?" (the default route fuses every step into the GEMM's prologue and
+   * epilogue). Any of them plans the batch on that path (SCUTE_E_UNSUPPORTED
+   * if it does not take the batch); results equal the default route's up to
+   * the order of fp32 additions. */
+  /* the GEMM writes x W only; s (applied inside the pass), b and the own
+   * low-rank term follow in an expand pass, the VeRA term in its own pass */
+  SCUTE_PLAN_ROUTE_EXPAND_PASS = 2,
+  /* with EXPAND_PASS: s applied by a pass of its own before the expand
+   * (s copied to every row, then multiplied into the output) */
+  SCUTE_PLAN_ROUTE_SEPARATE_S = 4,
+  /* the VeRA term in a pass of its own after the GEMM (whole batch, the
+   * shared B_sh read once per 32 VeRA rows) */
+  SCUTE_PLAN_ROUTE_VERA_PASS = 8,
+  /* the OFT rotation in a pass of its own before the prologue */
+  SCUTE_PLAN_ROUTE_ROTATE_PASS = 16
 } scute_plan_flag;
 
 /* scute_plan_batch with flags (a bitwise or of scute_plan_flag; 0 gives
  * scute_plan_batch). Errors as scute_plan_batch, plus SCUTE_E_INVALID for an
- * unknown flag bit. */
+ * unknown flag bit, SEPARATE_S without EXPAND_PASS, or DETERMINISTIC with a
+ * route bit, and SCUTE_E_UNSUPPORTED when a route bit is set and the batch
+ * does not fit the two-launch decode path. */
 scute_status scute_plan_batch_flags(scute_layer* layer, const int32_t* token_adapter,
                                     int32_t n, uint32_t flags, void* stream,
                                     scute_batch** out);
@@ -320,6 +339,14 @@ typedef struct scute_kernel_time {
  * the totals. */
 scute_status scute_profile_read(scute_layer* layer, scute_kernel_time* out, int32_t capacity,
                                 int32_t* count);
+
+/* Launch `count` empty kernels (one wave each) back to back on `stream`
+ * (null: default stream) on the current device, for the launch-cost term of
+ * the time model in "Where is the cheapest place to compute the remaining
+ * slots?" (added time = extra bytes / bandwidth + extra launches x launch
+ * cost): the caller times them with events. Errors: SCUTE_E_INVALID if
+ * count < 0; SCUTE_E_HIP if a launch fails. */
+scute_status scute_launch_empty(int32_t count, void* stream);
 
 /* Thread-local message of the last failed call on this thread ("" if none). */
 const char* scute_last_error(void);

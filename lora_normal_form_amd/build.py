@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HOST_SRCS = ["layer.cpp", "plan.cpp", "plan_decode.cpp", "plan_prefill.cpp", "plan_fdecode.cpp"]
-HIP_SRCS = ["forward.hip", "decode.hip", "prefill.hip", "fdecode.hip"]
+HIP_SRCS = ["forward.hip", "decode.hip", "prefill.hip", "fdecode.hip", "rotate.hip", "routes.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + os.path.join(ROOT, "include")]

@@ -975,6 +975,10 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   float* acc = D.acc32[D.fwd & 1];
   float* acc_next = D.acc32[(D.fwd + 1) & 1];
   int nl = 0;
+  if (D.route) {  // route variant: the rotation as a pass of its own
+    scute_status rs = launch_route_rotate(L, B, x, st, &nl);
+    if (rs != SCUTE_OK) return rs;
+  }
   {
     ProArgs pa{};
     pa.x = (const uint16_t*)x;
@@ -1044,6 +1048,10 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ++nl;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch k_decode_main");
+  if (D.route) {  // route variant: the passes after the GEMM
+    scute_status rs = launch_route_passes(L, B, y, acc, st, &nl);
+    if (rs != SCUTE_OK) return rs;
+  }
   if (launches) *launches = nl;
   return SCUTE_OK;
 }

@@ -5,12 +5,12 @@
 // explainer of "Scute: Exact Batched Serving for PEFT Adapters Beyond LoRA")
 // runs in at most two launches per forward:
 //
-// k_fd_rotate (only when some row rotates): delta = x (R - I) for the
-//   rotated rows, 4 rows by a run of columns per work-group, fp32
-//   accumulate, rounded once to bf16. The rotation comes before the shared
-//   GEMM, which then multiplies x and delta by the same W fragments ("Where
-//   is the cheapest place to compute the remaining slots?": rows are rotated
-//   by a kernel ahead of the GEMM and then share it).
+// k_fd_rotate (rotate.hip; only when some row rotates): delta = x (R - I)
+//   for the rotated rows, fp32 accumulate, rounded once to bf16. The
+//   rotation comes before the shared GEMM, which then multiplies x and delta
+//   by the same W fragments ("Where is the cheapest place to compute the
+//   remaining slots?": rows are rotated by a kernel ahead of the GEMM and
+//   then share it).
 //
 // k_fd_main, one work-group of 4 waves per (128-column tile, K slice):
 //   K loop   the base GEMM of the tile's 128 outputs over the slice for every
@@ -651,94 +651,6 @@ __global__ void __launch_bounds__(256, 1) k_fd_main(FdArgs a) {
                       a.cnt + (c * MG + g) * FWAVES + w, sst);
 }
 
-// ---------------------------------------------------------------------------
-// rotation
-// ---------------------------------------------------------------------------
-
-struct RotArgs {
-  const uint16_t* x;
-  const FdRotItem* items;
-  uint16_t* dx;
-  int32_t d_in;
-};
-
-// xor exchange inside groups of 32 lanes (ds_swizzle bit mode: and 0x1F,
-// xor MSK)
-template <int MSK>
-__device__ __forceinline__ float swz(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (MSK << 10) | 0x1F));
-}
-
-// One item: up to 4 rows of one adapter segment over NC columns (512, or 256
-// for blocks of 64). Column j of the block-diagonal (R - I) is stored as its
-// BLK values in a row, so the item's columns are one contiguous run of NC
-// BLK bf16: thread t loads 16-byte pieces 256 i + t of it (coalesced; piece
-// q is part q % PPC of column q / PPC), the rows' x over the same columns
-// goes to LDS, and each piece's 8-term dot product with the matching x part
-// is summed over the column's PPC lanes. The bf16 results gather in LDS and
-// leave as 16-byte row stores. Other block sizes (BLK = 0) take a scalar
-// loop per column.
-template <int BLK>
-__global__ void __launch_bounds__(256) k_fd_rotate(RotArgs a) {
-  constexpr int NC = BLK == 64 ? 256 : 512;
-  constexpr int PPC = BLK > 0 ? BLK / 8 : 1;
-  constexpr int NR = NC * PPC / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t sx[4][NC];
-  __shared__ __attribute__((aligned(16))) uint16_t so[4][NC];
-  const FdRotItem it = a.items[blockIdx.x];
-  const int t = threadIdx.x;
-  const int ncols = min(NC, a.d_in - it.c0);  // a multiple of 64
-  const int nr = it.n;
-  if constexpr (BLK > 0) {
-    const uint16_t* pg = it.P + (size_t)it.c0 * BLK;
-    uint4 pv[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int q = 256 * i + t;
-      pv[i] = q < ncols * PPC ? ldg16(pg + 8 * q) : make_uint4(0, 0, 0, 0);
-    }
-    {
-      const int r = t >> 6, pc = t & 63;
-      if (r < nr && 8 * pc < ncols)
-        *reinterpret_cast<uint4*>(&sx[r][8 * pc]) = ldg16(a.x + (size_t)it.tok[r] * a.d_in + it.c0 + 8 * pc);
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int q = 256 * i + t, col = q / PPC, p = q % PPC;
-      const int xo = col / BLK * BLK + 8 * p;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (r < nr) {
-          float v = dot8(*reinterpret_cast<const uint4*>(&sx[r][xo]), pv[i], 0.f);
-          if constexpr (PPC > 1) v += swz<1>(v);
-          if constexpr (PPC > 2) v += swz<2>(v);
-          if constexpr (PPC > 4) v += swz<4>(v);
-          if (p == 0 && col < ncols) so[r][col] = f2bf(v);
-        }
-    }
-  } else {
-    for (int col = t; col < ncols; col += 256) {
-      const int64_t cl = it.c0 + col;
-      const int64_t kb = cl / it.blk, jj = cl - kb * it.blk;
-      const uint16_t* pb = it.P + ((size_t)kb * it.blk + jj) * it.blk;
-      for (int r = 0; r < nr; ++r) {
-        const uint16_t* xr = a.x + (size_t)it.tok[r] * a.d_in + kb * it.blk;
-        float v = 0.f;
-        for (int i = 0; i < it.blk; ++i) v += bf2f(ldg(xr + i)) * bf2f(ldg(pb + i));
-        so[r][col] = f2bf(v);
-      }
-    }
-  }
-  lds_barrier();
-  for (int o = t; o < 4 * NC / 8; o += 256) {
-    const int r = o / (NC / 8), pc = o % (NC / 8);
-    if (r < nr && 8 * pc < ncols)
-      *(GLOBAL u32x4*)(a.dx + (size_t)(it.p0 + r) * a.d_in + it.c0 + 8 * pc) =
-          *reinterpret_cast<const u32x4*>(&so[r][8 * pc]);
-  }
-}
-
 template <int MGT>
 void launch_fd_main(const FdArgs& a, int grid, int nst, hipStream_t st) {
   switch (nst) {
@@ -756,20 +668,12 @@ scute_status launch_fdecode(scute_layer* L, const scute_batch* B, const void* x,
   const FdPlan& P = B->fp;
   int nl = 0;
   if (P.n_rot_items > 0) {
-    RotArgs ra{(const uint16_t*)x, P.rot, (uint16_t*)B->delta, (int32_t)L->d_in};
-    if (!ra.dx || !ra.items) return fail(SCUTE_E_STATE, "fused decode: rotation tables missing");
+    if (!B->delta || !P.rot) return fail(SCUTE_E_STATE, "fused decode: rotation tables missing");
     ProfScope ps(L, st, "fd_rotate");
-    const dim3 g(P.n_rot_items), b(256);
-    switch (P.rot_blk) {  // one block size per batch (else the scalar form)
-      case 8: hipLaunchKernelGGL(k_fd_rotate<8>, g, b, 0, st, ra); break;
-      case 16: hipLaunchKernelGGL(k_fd_rotate<16>, g, b, 0, st, ra); break;
-      case 32: hipLaunchKernelGGL(k_fd_rotate<32>, g, b, 0, st, ra); break;
-      case 64: hipLaunchKernelGGL(k_fd_rotate<64>, g, b, 0, st, ra); break;
-      default: hipLaunchKernelGGL(k_fd_rotate<0>, g, b, 0, st, ra); break;
-    }
+    scute_status rs = launch_rotate_items(P.rot, P.n_rot_items, P.rot_blk, (const uint16_t*)x,
+                                          (uint16_t*)B->delta, (int32_t)L->d_in, st);
+    if (rs != SCUTE_OK) return rs;
     ++nl;
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "launch k_fd_rotate");
   }
   FdArgs a{};
   a.x = (const uint16_t*)x;

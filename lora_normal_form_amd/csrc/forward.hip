@@ -316,7 +316,7 @@ int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
   (void)L;
   if (B->n == 0) return 0;
   if (B->fp.enabled) return (B->fp.n_rot_items > 0) + 1;  // rotation + fused main
-  if (B->dp.enabled) return 2;  // prologue (gather, rotation, shrinks) + main
+  if (B->dp.enabled) return 2 + decode_route_launches(B);  // prologue (gather, rotation, shrinks) + main
   if (B->pp.enabled) return (B->pp.n_pro > 0) + 1;  // prologue (rotation, shrinks) + main
   return (B->n_rot > 0) + (B->max_rank > 0) + (B->n_vera > 0) + 1 +
          (B->max_rank > 0 || B->n_vera > 0);
@@ -356,6 +356,19 @@ extern "C" scute_status scute_layer_forward(scute_layer* L, const scute_batch* B
   scute_status st = launch_forward(L, B, x, W, y, (hipStream_t)stream, nullptr);
   if (prev != L->device && prev >= 0) (void)hipSetDevice(prev);
   return st;
+}
+
+namespace scute {
+__global__ void k_empty() {}
+}  // namespace scute
+
+extern "C" scute_status scute_launch_empty(int32_t count, void* stream) {
+  using namespace scute;
+  if (count < 0) return fail(SCUTE_E_INVALID, "scute_launch_empty: count must be >= 0");
+  for (int32_t i = 0; i < count; ++i) hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "scute_launch_empty");
+  return SCUTE_OK;
 }
 
 extern "C" scute_status scute_profile_enable(scute_layer* L, int32_t enable) {

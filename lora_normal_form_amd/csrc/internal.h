@@ -133,6 +133,12 @@ struct DecVeraRow {
   int32_t p;
 };
 
+struct FdRotItem;
+// Route-pass chunk: sorted rows p0 .. p0 + n - 1 (n <= 16) of adapter a.
+struct RtChunk {
+  int32_t p0, n, a, pad;
+};
+
 struct DecodePlan {
   bool enabled = false;
   int32_t MG = 0;       // row groups of 32 covering the n sorted rows
@@ -168,6 +174,13 @@ struct DecodePlan {
   // forwards launched with this plan; the shrink sums alternate between the
   // two acc32 buffers, and each forward's prologue clears the other one
   mutable uint32_t fwd = 0;
+  // route variant (SCUTE_PLAN_ROUTE_* bits; 0: everything fused)
+  uint32_t route = 0;
+  const FdRotItem* rot = nullptr;  // rotation pass items (ROTATE_PASS)
+  int32_t n_rot_items = 0, rot_blk = 0;
+  const RtChunk* chunks = nullptr;  // expand pass chunks (EXPAND_PASS)
+  int32_t n_chunks = 0;
+  float* S_rows = nullptr;          // [n][d_out] s copied to every row (SEPARATE_S)
 };
 
 // ---- fused decode path (fdecode.hip / plan_fdecode.cpp) --------------------
@@ -383,6 +396,21 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
 scute_status build_fdecode_plan(const scute_layer* L, scute_batch* B, hipStream_t st);
 scute_status launch_fdecode(scute_layer* L, const scute_batch* B, const void* x, const void* W,
                             float* y, hipStream_t st, int32_t* launches);
+
+// route passes of the decode path (routes.hip)
+constexpr uint32_t ROUTE_MASK = SCUTE_PLAN_ROUTE_EXPAND_PASS | SCUTE_PLAN_ROUTE_SEPARATE_S |
+                                SCUTE_PLAN_ROUTE_VERA_PASS | SCUTE_PLAN_ROUTE_ROTATE_PASS;
+int32_t decode_route_launches(const scute_batch* B);
+scute_status launch_route_rotate(scute_layer* L, const scute_batch* B, const void* x, hipStream_t st,
+                                 int32_t* nl);
+scute_status launch_route_passes(scute_layer* L, const scute_batch* B, float* y, const float* acc,
+                                 hipStream_t st, int32_t* nl);
+
+// rotation pass (rotate.hip): items of up to 4 rows by 512 columns (256 for
+// blocks of 64); blk the block size shared by every item, or 0 for mixed
+// sizes (scalar form)
+scute_status launch_rotate_items(const FdRotItem* items, int32_t n_items, int32_t blk, const uint16_t* x,
+                                 uint16_t* dx, int32_t d_in, hipStream_t st);
 
 // prefill path (prefill.hip / plan_prefill.cpp)
 scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_t st);

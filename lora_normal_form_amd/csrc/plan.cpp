@@ -59,8 +59,14 @@ extern "C" scute_status scute_plan_batch_flags(scute_layer* L, const int32_t* to
   try {
     if (!L || !out) return fail(SCUTE_E_INVALID, "scute_plan_batch: null argument");
     *out = nullptr;
-    if (flags & ~(uint32_t)SCUTE_PLAN_DETERMINISTIC)
+    if (flags & ~((uint32_t)SCUTE_PLAN_DETERMINISTIC | ROUTE_MASK))
       return fail(SCUTE_E_INVALID, "scute_plan_batch_flags: unknown flag bits");
+    if ((flags & SCUTE_PLAN_ROUTE_SEPARATE_S) && !(flags & SCUTE_PLAN_ROUTE_EXPAND_PASS))
+      return fail(SCUTE_E_INVALID, "scute_plan_batch_flags: ROUTE_SEPARATE_S needs ROUTE_EXPAND_PASS");
+    if ((flags & SCUTE_PLAN_DETERMINISTIC) && (flags & ROUTE_MASK))
+      return fail(SCUTE_E_INVALID, "scute_plan_batch_flags: route variants are not deterministic");
+    if ((flags & ROUTE_MASK) && L->device < 0)
+      return fail(SCUTE_E_UNSUPPORTED, "scute_plan_batch_flags: route variants need a device layer");
     if (n < 0 || n > (1 << 22)) return fail(SCUTE_E_SHAPE, "scute_plan_batch: n must be in [0, 2^22]");
     if (n > 0 && !token_adapter) return fail(SCUTE_E_INVALID, "scute_plan_batch: token_adapter is null");
     for (int32_t t = 0; t < n; ++t) {
@@ -163,9 +169,17 @@ extern "C" scute_status scute_plan_batch_flags(scute_layer* L, const int32_t* to
         delete B;
         return hip_fail(e, "plan upload / workspace");
       }
-      scute_status ds = build_fdecode_plan(L, B, s);
-      if (ds == SCUTE_OK && !B->fp.enabled) ds = build_decode_plan(L, B, s);
-      if (ds == SCUTE_OK && !B->fp.enabled && !B->dp.enabled) ds = build_prefill_plan(L, B, s);
+      scute_status ds = SCUTE_OK;
+      if (flags & ROUTE_MASK) {
+        ds = build_decode_plan(L, B, s);
+        if (ds == SCUTE_OK && !B->dp.enabled)
+          ds = fail(SCUTE_E_UNSUPPORTED, "scute_plan_batch_flags: route variants need a batch the "
+                                         "two-launch decode path takes (bf16, up to 256 rows)");
+      } else {
+        ds = build_fdecode_plan(L, B, s);
+        if (ds == SCUTE_OK && !B->fp.enabled) ds = build_decode_plan(L, B, s);
+        if (ds == SCUTE_OK && !B->fp.enabled && !B->dp.enabled) ds = build_prefill_plan(L, B, s);
+      }
       restore();
       if (ds != SCUTE_OK) {
         free_batch_memory(B);

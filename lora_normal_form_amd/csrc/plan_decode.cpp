@@ -44,7 +44,13 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const int64_t d_in = L->d_in, d_out = L->d_out;
   // the two-launch decode path (gather / rotation / shrink prologue, then
   // the GEMM): SCUTE_DECODE=2
-  if (env_int("SCUTE_DECODE", DECODE_DEFAULT) != 2 || (B->flags & SCUTE_PLAN_DETERMINISTIC)) return SCUTE_OK;
+  // (route variants always plan here)
+  const uint32_t route = B->flags & ROUTE_MASK;
+  if (!route && (env_int("SCUTE_DECODE", DECODE_DEFAULT) != 2 || (B->flags & SCUTE_PLAN_DETERMINISTIC)))
+    return SCUTE_OK;
+  const bool rot_in_pro = !(route & SCUTE_PLAN_ROUTE_ROTATE_PASS);
+  const bool own_fused = !(route & SCUTE_PLAN_ROUTE_EXPAND_PASS);
+  const bool vera_fused = !(route & (SCUTE_PLAN_ROUTE_EXPAND_PASS | SCUTE_PLAN_ROUTE_VERA_PASS));
   if (L->act != SCUTE_BF16 || n <= 0 || n > 256) return SCUTE_OK;
   // K parts of the shrinks: at most 8 of 1024 (own) and 16 of 512 (VeRA)
   if (d_in % 128 != 0 || d_in > 8192 || d_out % 64 != 0) return SCUTE_OK;
@@ -87,7 +93,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
-    if (E.flags & F_R) n_rot_items += (len + 3) / 4 * (int32_t)(d_in / 64);
+    if ((E.flags & F_R) && rot_in_pro) n_rot_items += (len + 3) / 4 * (int32_t)(d_in / 64);
     if (E.flags & F_TERM) n_sgroups += (len + 3) / 4 * ((E.rank + 3) / 4);
   }
   const int32_t KQ = (int32_t)((d_in + 1023) / 1024);
@@ -117,7 +123,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
-    if (!(E.flags & F_TERM)) continue;
+    if (!(E.flags & F_TERM) || !own_fused) continue;
     for (int32_t g = start / 32; g * 32 < start + len; ++g) {
       const int32_t lo = std::max(start, 32 * g), hi = std::min(start + len, 32 * g + 32);
       for (int32_t k = 0; k < E.rank; k += 64)
@@ -128,7 +134,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   // The VeRA term can run dense when a slice has at most 256 ranks of it and
   // the VeRA rows' groups fit the LDS buffer the kernel stages them in, 128
   // ranks at a time (32 (gv1 - gv0) rows of 256 bytes, at most 256 rows).
-  if (B->n_vera > 0) {
+  if (B->n_vera > 0 && vera_fused) {
     int32_t pmin = n, pmax = -1;
     for (int32_t v : B->vera_pos) {
       pmin = std::min(pmin, v);
@@ -148,7 +154,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
       D.gv1 = gv1;
     }
   }
-  if (B->n_vera > 0 && D.gv1 == D.gv0) {
+  if (B->n_vera > 0 && vera_fused && D.gv1 == D.gv0) {
     for (int32_t g = 0; g < D.MG; ++g) {
       bool any = false;
       for (int32_t p = 32 * g; p < std::min(n, 32 * g + 32); ++p) any |= row_vera[p] != 0;
@@ -210,6 +216,41 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const size_t o_steps = take(sizeof(DecStep) * steps.size() + 16);
   const size_t o_goff = take(sizeof(int32_t) * goff.size());
   const size_t o_ones = take(4 * (size_t)d_out);
+  // route tables: rotation pass items, expand pass chunks
+  std::vector<FdRotItem> rot;
+  std::vector<RtChunk> chunks;
+  int32_t rot_blk = -1;
+  for (int32_t i = 0; i < B->nseg(); ++i) {
+    const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
+    const SlotEntry& E = L->table[a];
+    if ((E.flags & F_R) && !rot_in_pro) rot_blk = rot_blk == -1 ? E.blk : (rot_blk == E.blk ? rot_blk : 0);
+    const bool exp_rows = (route & SCUTE_PLAN_ROUTE_EXPAND_PASS) &&
+                          ((E.flags & (F_B | F_TERM)) ||
+                           ((E.flags & F_S) && !(route & SCUTE_PLAN_ROUTE_SEPARATE_S)));
+    if (exp_rows)
+      for (int32_t r0 = 0; r0 < len; r0 += 16) chunks.push_back(RtChunk{start + r0, std::min(16, len - r0), a, 0});
+  }
+  if (rot_blk != 8 && rot_blk != 16 && rot_blk != 32 && rot_blk != 64) rot_blk = 0;
+  const int64_t rot_cols = rot_blk == 64 ? 256 : 512;
+  if (!rot_in_pro)
+    for (int32_t i = 0; i < B->nseg(); ++i) {
+      const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
+      const SlotEntry& E = L->table[a];
+      if (!(E.flags & F_R)) continue;
+      for (int32_t r0 = 0; r0 < len; r0 += 4)
+        for (int64_t c0 = 0; c0 < d_in; c0 += rot_cols) {
+          FdRotItem it{};
+          it.p0 = start + r0;
+          it.n = std::min(4, len - r0);
+          it.c0 = (int32_t)c0;
+          it.blk = E.blk;
+          for (int32_t r = 0; r < 4; ++r) it.tok[r] = B->perm[it.p0 + std::min(r, it.n - 1)];
+          it.P = (const uint16_t*)E.P;
+          rot.push_back(it);
+        }
+    }
+  const size_t o_rot = take(sizeof(FdRotItem) * rot.size() + 16);
+  const size_t o_chunks = take(sizeof(RtChunk) * chunks.size() + 16);
   const size_t tables = o;
   const size_t o_zeros = take(4 * (size_t)d_out);
   const size_t acc_bytes = 4 * (size_t)D.M_pad * D.AW;
@@ -222,6 +263,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const size_t o_xs = take(xs_bytes);
   const size_t o_acc0 = take(acc_bytes), o_acc1 = take(acc_bytes);
   const size_t o_part = take(part_bytes), o_cnt = take(4 * (size_t)D.C);
+  const size_t o_srows = take((route & SCUTE_PLAN_ROUTE_SEPARATE_S) ? 4 * (size_t)n * d_out : 0);
   const size_t total = o;
 
   hipError_t e = hipMalloc(&B->fast_dev, total);
@@ -237,9 +279,11 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     const int32_t a = B->row_adapter[p];
     if (a < 0) continue;
     const SlotEntry& E = L->table[a];
-    if (E.flags & F_S) rows[p].s = E.s;
-    if (E.flags & F_B) rows[p].b = E.b;
-    if (E.flags & F_VERA) {
+    // (the expand pass route applies s and b after the GEMM; the VeRA pass
+    // routes add the VeRA term after it)
+    if ((E.flags & F_S) && own_fused) rows[p].s = E.s;
+    if ((E.flags & F_B) && own_fused) rows[p].b = E.b;
+    if ((E.flags & F_VERA) && vera_fused) {
       rows[p].e = E.ve;
       rows[p].flags = 1;
     }
@@ -263,7 +307,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
-    if (E.flags & F_R)
+    if ((E.flags & F_R) && rot_in_pro)
       for (int32_t r0 = 0; r0 < len; r0 += 4)
         for (int64_t c0 = 0; c0 < d_in; c0 += 64) {
           DecProItem it{};
@@ -344,6 +388,8 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   if (!vrows.empty()) memcpy(h.data() + o_vrows, vrows.data(), sizeof(DecVeraRow) * vrows.size());
   if (!steps.empty()) memcpy(h.data() + o_steps, steps.data(), sizeof(DecStep) * steps.size());
   memcpy(h.data() + o_goff, goff.data(), sizeof(int32_t) * goff.size());
+  if (!rot.empty()) memcpy(h.data() + o_rot, rot.data(), sizeof(FdRotItem) * rot.size());
+  if (!chunks.empty()) memcpy(h.data() + o_chunks, chunks.data(), sizeof(RtChunk) * chunks.size());
   for (int64_t j = 0; j < d_out; ++j) {
     const float one = 1.0f;
     memcpy(h.data() + o_ones + 4 * j, &one, 4);
@@ -375,6 +421,13 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   D.acc_bytes = (uint32_t)acc_bytes;
   D.part_bytes = (uint32_t)part_bytes;
   D.fwd = 0;
+  D.route = route;
+  D.rot = rot.empty() ? nullptr : (const FdRotItem*)(d + o_rot);
+  D.n_rot_items = (int32_t)rot.size();
+  D.rot_blk = rot_blk;
+  D.chunks = chunks.empty() ? nullptr : (const RtChunk*)(d + o_chunks);
+  D.n_chunks = (int32_t)chunks.size();
+  D.S_rows = (route & SCUTE_PLAN_ROUTE_SEPARATE_S) ? (float*)(d + o_srows) : nullptr;
   D.enabled = true;
   return SCUTE_OK;
 }

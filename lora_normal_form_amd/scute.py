@@ -91,6 +91,7 @@ SIGNATURES = {
     "scute_profile_enable": (C.c_int32, [_P, C.c_int32]),
     "scute_profile_read": (C.c_int32, [_P, C.POINTER(KernelTime), C.c_int32,
                                        C.POINTER(C.c_int32)]),
+    "scute_launch_empty": (C.c_int32, [C.c_int32, _P]),
     "scute_last_error": (C.c_char_p, []),
     "scute_version": (C.c_char_p, []),
 }
@@ -177,6 +178,10 @@ def scute_unload_adapter(layer: int, id: int, stream=None) -> None:
 
 
 PLAN_DETERMINISTIC = 1
+PLAN_ROUTE_EXPAND_PASS = 2
+PLAN_ROUTE_SEPARATE_S = 4
+PLAN_ROUTE_VERA_PASS = 8
+PLAN_ROUTE_ROTATE_PASS = 16
 
 
 def scute_plan_batch(layer: int, token_adapter, stream=None) -> int:
@@ -193,6 +198,10 @@ def scute_plan_batch_flags(layer: int, token_adapter, flags: int, stream=None) -
     _check(lib.scute_plan_batch_flags(layer, ta.ctypes.data if ta.size else None, int(ta.size),
                                       int(flags), _stream_ptr(stream), C.byref(h)))
     return h.value
+
+
+def scute_launch_empty(count: int, stream=None) -> None:
+    _check(lib.scute_launch_empty(int(count), _stream_ptr(stream)))
 
 
 def scute_batch_destroy(batch: int) -> None:
@@ -332,9 +341,10 @@ class Layer:
     def unload(self, id, stream=None):
         scute_unload_adapter(self.h, id, stream)
 
-    def plan(self, token_adapter, stream=None, deterministic=False) -> "Batch":
-        if deterministic:
-            return Batch(self, scute_plan_batch_flags(self.h, token_adapter, PLAN_DETERMINISTIC, stream))
+    def plan(self, token_adapter, stream=None, deterministic=False, flags=0) -> "Batch":
+        flags |= PLAN_DETERMINISTIC if deterministic else 0
+        if flags:
+            return Batch(self, scute_plan_batch_flags(self.h, token_adapter, flags, stream))
         return Batch(self, scute_plan_batch(self.h, token_adapter, stream))
 
     def forward(self, batch, x, W, y, stream=None):

@@ -60,12 +60,12 @@ class Loaded:
 
 
 def load(wl, device=0, max_adapters: Optional[int] = None, plan: bool = True,
-         shared=None, deterministic: bool = False) -> Loaded:
+         shared=None, deterministic: bool = False, flags: int = 0) -> Loaded:
     """Create a layer on ``device``, load every adapter, plan the batch.
 
     ``shared``: optional (x, W, A_sh, B_sh) device tensors to reuse instead of
     uploading new copies. ``deterministic``: plan with bit-repeatable
-    forwards (SCUTE_PLAN_DETERMINISTIC).
+    forwards (SCUTE_PLAN_DETERMINISTIC); ``flags``: other scute_plan_flag bits.
     """
     import torch
     dev = torch.device("cuda", device) if device >= 0 else None
@@ -86,5 +86,5 @@ def load(wl, device=0, max_adapters: Optional[int] = None, plan: bool = True,
         kw = adapter_arrays(wl, a)
         L.load(a.id, **kw)
     y = torch.empty((wl.n, wl.d_out), dtype=torch.float32, device=dev)
-    B = L.plan(wl.token_adapter, deterministic=deterministic) if plan else None
+    B = L.plan(wl.token_adapter, deterministic=deterministic, flags=flags) if plan else None
     return Loaded(L, B, x, W, y, A_sh, B_sh)

@@ -277,3 +277,38 @@ def test_plan_outlives_its_layer():
         b.close()
         assert L2.cost(L2.plan([0, 0]))["bytes"] > 0
         L2.close()
+
+
+def test_plan_flags_are_validated():
+    # unknown bits, SEPARATE_S without EXPAND_PASS and DETERMINISTIC with a
+    # route bit are refused; route variants need a device layer
+    wl = make_config(0)
+    ld = glue.load(wl, device=-1, plan=False)
+    ta = wl.token_adapter
+    bad = [(1 << 9, scute.E_INVALID),
+           (scute.PLAN_ROUTE_SEPARATE_S, scute.E_INVALID),
+           (scute.PLAN_DETERMINISTIC | scute.PLAN_ROUTE_VERA_PASS, scute.E_INVALID),
+           (scute.PLAN_ROUTE_ROTATE_PASS, scute.E_UNSUPPORTED)]
+    for flags, code in bad:
+        with pytest.raises(scute.ScuteError) as ei:
+            ld.layer.plan(ta, flags=flags)
+        assert ei.value.code == code, (flags, ei.value)
+    b = ld.layer.plan(ta, flags=scute.PLAN_DETERMINISTIC)  # host plan: fine
+    b.close()
+
+
+def test_route_extra_bytes_by_hand():
+    # 128 rows of 4096 fp32 outputs: one pass over y is 2 x 128 x 16 KB
+    row = 4 * 4096
+    b, l = costmodel.route_extra("expand_pass", n=128, d_out=4096, exp_rows=100, vera_rows=20)
+    assert (b, l) == (2 * row * 120, 2)
+    b, l = costmodel.route_extra("expand_pass", n=128, d_out=4096, exp_rows=0, vera_rows=20)
+    assert (b, l) == (2 * row * 20, 1)
+    # copy: 40 rows read s, all 128 rows write S; multiply: y, S read and y
+    # written for 128 rows; 5 chunks no longer read s in the expand
+    b, l = costmodel.route_extra("separate_s", n=128, d_out=4096, s_rows=40, s_chunks=5)
+    assert (b, l) == (row * (40 + 128 + 3 * 128 - 5), 2)
+    assert costmodel.route_extra("vera_pass", n=128, d_out=4096, vera_rows=0) == (0.0, 0)
+    assert costmodel.route_extra("rotate_pass", n=128, d_out=4096, rot_rows=26) == (0.0, 1)
+    with pytest.raises(ValueError):
+        costmodel.route_extra("nope", n=1, d_out=1)
