@@ -276,8 +276,10 @@ scute_status scute_cost_model(const scute_layer* layer, const scute_batch* batch
 /* ---- introspection (tests, debugging) ---------------------------------- */
 
 typedef enum scute_slot {
-  SCUTE_SLOT_A = 0,  /* folded A' [rank][d_in]        activation dtype */
-  SCUTE_SLOT_B = 1,  /* folded B' [d_out][rank]       activation dtype */
+  SCUTE_SLOT_A = 0,  /* folded A' [rank8][d_in]       activation dtype */
+  SCUTE_SLOT_B = 1,  /* folded B' [d_out][rank8]      activation dtype
+                        (rank8: the rank rounded up to a multiple of 8;
+                        the added rows of A' and columns of B' are zero) */
   SCUTE_SLOT_S = 2,  /* live s [d_out]                float32          */
   SCUTE_SLOT_BIAS = 3, /* b [d_out]                   float32          */
   SCUTE_SLOT_VD = 4, /* VeRA d [r_v]                  float32          */
@@ -290,7 +292,7 @@ typedef enum scute_slot {
 typedef struct scute_adapter_info {
   int32_t loaded;
   int32_t method;
-  int32_t rank;
+  int32_t rank;  /* stored rank: the own term's rank rounded up to 8 (0: none) */
   int32_t blk;
   int32_t has_R, has_s, has_b, has_term, has_vera;
 } scute_adapter_info;

@@ -376,14 +376,19 @@ scute_status fold_adapter(const scute_layer* L, const scute_adapter_desc* D, con
       F.s.resize(d_out);
       for (int64_t j = 0; j < d_out; ++j) F.s[j] = (float)s64[j];
     }
-    F.A.resize((size_t)r * d_in * es);
-    F.B.resize((size_t)d_out * r * es);
+    // stored at the rank rounded up to a multiple of 8: the added A' rows and
+    // B' columns are zero, so the term is unchanged and every kernel's rank
+    // steps cover whole 8-rank pieces
+    const int32_t r8 = (r + 7) / 8 * 8;
+    F.rank = r8;
+    F.A.assign((size_t)r8 * d_in * es, 0);
+    F.B.assign((size_t)d_out * r8 * es, 0);
     for (int32_t k = 0; k < r; ++k)
       for (int64_t i = 0; i < d_in; ++i)
         store_act(F.A.data(), act, (size_t)k * d_in + i, D->c * dvec[k] * A64[(size_t)k * d_in + i]);
     for (int64_t j = 0; j < d_out; ++j)
       for (int32_t k = 0; k < r; ++k)
-        store_act(F.B.data(), act, (size_t)j * r + k, B64[(size_t)j * r + k] * evec[j]);
+        store_act(F.B.data(), act, (size_t)j * r8 + k, B64[(size_t)j * r + k] * evec[j]);
     F.flags |= F_TERM;
   }
 

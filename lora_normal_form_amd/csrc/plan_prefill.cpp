@@ -39,8 +39,9 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   const int64_t d_in = L->d_in, d_out = L->d_out;
   if (env_int("SCUTE_PREFILL", 1) == 0) return SCUTE_OK;
   if (L->act != SCUTE_BF16 || n <= 0) return SCUTE_OK;
-  // the main kernel's K loop is unrolled for 64 stages of 64
-  if (d_in != 4096 || d_out % 256 != 0) return SCUTE_OK;
+  // the main kernel's K loop runs in stages of 64 k (unrolled at compile
+  // time for d_in 4096); the prologue's items need d_in % 256 (checked below)
+  if (d_in % 64 != 0 || d_out % 256 != 0) return SCUTE_OK;
   // W, x and the Delta rows are addressed through buffer ranges with 32-bit offsets
   if (d_in * d_out * 2 >= ((int64_t)1 << 32) || (int64_t)n * d_in * 2 >= ((int64_t)1 << 32))
     return SCUTE_OK;
@@ -146,10 +147,12 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
     rest.insert(rest.end(), lst.begin() + nf, lst.end());
   }
   int32_t parts = 1;
-  while (parts < 4 && !rest.empty() && (int64_t)rest.size() * parts * 2 <= cu) parts *= 2;
+  const int64_t nst = d_in / 64;
+  while (parts < 4 && !rest.empty() && (int64_t)rest.size() * parts * 2 <= cu && nst % (parts * 2) == 0)
+    parts *= 2;
   parts = env_int("SCUTE_PREFILL_PARTS", parts);
-  if (parts != 1 && parts != 2 && parts != 4)
-    return fail(SCUTE_E_INVALID, "bad SCUTE_PREFILL_PARTS (1, 2 or 4)");
+  if ((parts != 1 && parts != 2 && parts != 4) || nst % parts != 0)
+    return fail(SCUTE_E_INVALID, "bad SCUTE_PREFILL_PARTS (1, 2 or 4 dividing d_in / 64)");
   std::vector<int4> items;
   for (size_t j = 0;; ++j) {
     bool any = false;
@@ -171,7 +174,7 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   // shrink tiles of 64 rows x 64 ranks over one K part of 1024 (own: per
   // segment; VeRA: over the table of VeRA rows), then rotation tiles of 32
   // rows x 256 columns
-  const int32_t KP = (int32_t)(d_in / 1024);
+  const int32_t KP = (int32_t)((d_in + 1023) / 1024);  // the last part may be shorter
   std::vector<PfProItem> pro;
   int32_t n_tiles = 0;  // shrink tiles (each with an arrival counter)
   for (int32_t i = 0; i < B->nseg(); ++i) {
@@ -212,6 +215,12 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
                                   (const uint16_t*)E.P, E.blk, 0});
   }
   P.n_pro = (int32_t)pro.size();
+  // the prologue's items work in slices (shrinks) and column runs
+  // (rotation) of 256
+  if (P.n_pro > 0 && d_in % 256 != 0) {
+    P = PrefillPlan{};
+    return SCUTE_OK;
+  }
 
   // ---- one device allocation: tables, then the shrink sums ----------------------
   size_t o = 0;

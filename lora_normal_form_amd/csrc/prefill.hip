@@ -1,5 +1,6 @@
 // MFMA prefill path (bf16 activations, fp32 accumulate, long adapter
-// segments; d_in = 4096).
+// segments; d_in a multiple of 64, and of 256 when a row rotates or has a
+// low-rank term).
 //
 // Two kernels per forward.
 //
@@ -64,6 +65,7 @@ struct PfArgs {
   int32_t* cnt;             // [n_split] arrival counters, kept at zero between forwards
   uint32_t acc_bytes, x_bytes, dx_bytes, part_bytes;
   int32_t d_in, d_out, RT, AW, r_v, P;
+  int32_t nst;  // 64-k stages of the whole K dimension (d_in / 64)
 };
 
 constexpr int PK = 64;              // k per stage
@@ -243,6 +245,24 @@ __device__ __forceinline__ void pf_produce(const PfSrc (&src)[4], uint8_t* s0, u
   }
 }
 
+// Consumer side for a stage count known only at run time: the same steps,
+// three per round so every slot stays a distinct LDS object
+__device__ __forceinline__ void pf_cloop(int nst, uint8_t* s0, uint8_t* s1, uint8_t* s2,
+                                         f32x16 (&acc)[4][2], int m, int h, int w) {
+  for (int t = 0; t < nst; t += 3) {
+    wg_barrier();
+    pf_mma<false>(s0, acc, m, h, w);
+    if (t + 1 < nst) {
+      wg_barrier();
+      pf_mma<false>(s1, acc, m, h, w);
+    }
+    if (t + 2 < nst) {
+      wg_barrier();
+      pf_mma<false>(s2, acc, m, h, w);
+    }
+  }
+}
+
 // the K loop over NST stages: the first two stages, then the pipeline steps
 template <int NST>
 __device__ __forceinline__ void pf_kloop(const PfSrc& src, uint8_t* s0, uint8_t* s1, uint8_t* s2,
@@ -266,7 +286,7 @@ __device__ __forceinline__ uint4 scale_bf8(uint4 v, float e) {
 }
 
 // NST: stages of the whole K dimension (a K part of a split tile covers
-// NST / P of them)
+// NST / P of them); 0: the count a.nst, known at run time
 // Five waves: waves 0..3 multiply (and run the epilogue), wave 4 issues the
 // K loop's loads and leaves after the loop.
 template <int NST>
@@ -289,6 +309,7 @@ k_prefill_main(PfArgs a) {
   const int64_t col0 = (int64_t)c * 256 + 64 * w + m;  // column block cb: col0 + 32 cb
   const PfChunk ch = a.chunks[ci];
   const GLOBAL int32_t* cr = (const GLOBAL int32_t*)(a.crow + (size_t)ci * 128);
+  const int nst_all = NST > 0 ? NST : a.nst;
 
   // (0) the producer wave: sources of every consumer's pieces, then the loads
   if (w == 4) {
@@ -307,9 +328,9 @@ k_prefill_main(PfArgs a) {
       }
       srcv[v].woff = (uint32_t)(((int64_t)(8 * v + (lane >> 3)) * d_in + 8 * piece) * 2);
       srcv[v].wstep = (uint32_t)(32 * d_in * 2);
-      srcv[v].kb = kp < 0 ? 0 : kp * (NST / a.P) * PK * 2;
+      srcv[v].kb = kp < 0 ? 0 : kp * (nst_all / a.P) * PK * 2;
     }
-    pf_produce(srcv, slot0, slot1, slot2, kp < 0 ? NST : NST / a.P);
+    pf_produce(srcv, slot0, slot1, slot2, kp < 0 ? nst_all : nst_all / a.P);
     return;
   }
 
@@ -329,12 +350,16 @@ k_prefill_main(PfArgs a) {
   for (int g = 0; g < 4; ++g)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[g][cb] = f32x16{};
-  if (kp < 0)
-    pf_csteps<NST, 0>(slot0, slot1, slot2, acc, m, h, w);
-  else if (a.P == 4)
-    pf_csteps<NST / 4, 0>(slot0, slot1, slot2, acc, m, h, w);
-  else
-    pf_csteps<NST / 2, 0>(slot0, slot1, slot2, acc, m, h, w);
+  if constexpr (NST > 0) {
+    if (kp < 0)
+      pf_csteps<NST, 0>(slot0, slot1, slot2, acc, m, h, w);
+    else if (a.P == 4)
+      pf_csteps<NST / 4, 0>(slot0, slot1, slot2, acc, m, h, w);
+    else
+      pf_csteps<NST / 2, 0>(slot0, slot1, slot2, acc, m, h, w);
+  } else {
+    pf_cloop(kp < 0 ? nst_all : nst_all / a.P, slot0, slot1, slot2, acc, m, h, w);
+  }
   lds_barrier();  // every wave is done with the ring
 
   // (4b) the P parts of a split tile meet: each stores its partial tile with
@@ -635,9 +660,12 @@ __global__ void __launch_bounds__(256) k_prefill_prologue(PpArgs a) {
   const rsrc_t rx = make_rsrc(a.x, a.x_bytes);
   const rsrc_t ra = vera ? make_rsrc(a.A_sh, a.ash_bytes)
                          : make_rsrc(it.ptr, (uint32_t)((int64_t)(k0 + nk) * d_in * 2));
+  // slices of 256 in this part (the last part of a d_in that is not a
+  // multiple of 1024 has fewer than 4)
+  const int ns = min(4, (int)((d_in - kbase) / 256));
   issue_fence();
   pp_stage(buf0, rx, ra, xoff, aoff, kbase * 2, w);
-  pp_stage(buf1, rx, ra, xoff, aoff, (kbase + 256) * 2, w);
+  if (ns > 1) pp_stage(buf1, rx, ra, xoff, aoff, (kbase + 256) * 2, w);
   issue_fence();
   // VeRA: rows and d of this lane's outputs, fetched while the loads land
   const int rb = w & 1, cb = w >> 1;
@@ -651,24 +679,40 @@ __global__ void __launch_bounds__(256) k_prefill_prologue(PpArgs a) {
       dsc[i] = ldg(o.vd + k0 + 32 * cb + m);
     }
   }
-  // (2) four slices, two buffers
+  // (2) up to four slices, two buffers; each wait lets only the slice
+  //     staged after the one it waits for stay in flight
   f32x16 acc = {};
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+  if (ns > 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   wg_barrier();
   pp_mul(buf0, acc, rb, cb, m, h);
-  wg_barrier();
-  pp_stage(buf0, rx, ra, xoff, aoff, (kbase + 512) * 2, w);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
-  wg_barrier();
-  pp_mul(buf1, acc, rb, cb, m, h);
-  wg_barrier();
-  pp_stage(buf1, rx, ra, xoff, aoff, (kbase + 768) * 2, w);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
-  wg_barrier();
-  pp_mul(buf0, acc, rb, cb, m, h);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  wg_barrier();
-  pp_mul(buf1, acc, rb, cb, m, h);
+  if (ns > 1) {
+    wg_barrier();
+    if (ns > 2) pp_stage(buf0, rx, ra, xoff, aoff, (kbase + 512) * 2, w);
+    if (ns > 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    wg_barrier();
+    pp_mul(buf1, acc, rb, cb, m, h);
+    if (ns > 2) {
+      wg_barrier();
+      if (ns > 3) pp_stage(buf1, rx, ra, xoff, aoff, (kbase + 768) * 2, w);
+      if (ns > 3)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(PP_LOADS));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      wg_barrier();
+      pp_mul(buf0, acc, rb, cb, m, h);
+      if (ns > 3) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        wg_barrier();
+        pp_mul(buf1, acc, rb, cb, m, h);
+      }
+    }
+  }
   const int j = 32 * cb + m;  // rank of this lane's outputs within the tile
   // (3) store this K part's partial tile (VeRA: scaled by d, which is per
   //     rank and so commutes with the K sum): element i of wave w, lane l
@@ -751,7 +795,7 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
     pa.tbf = P.tbf;
     pa.tcnt = P.tcnt;
     pa.tbf_bytes = P.tbf_bytes;
-    pa.KP = (int32_t)(L->d_in / 1024);
+    pa.KP = (int32_t)((L->d_in + 1023) / 1024);
     pa.x_bytes = (uint32_t)((size_t)B->n * L->d_in * 2);
     pa.ash_bytes = (uint32_t)((size_t)L->r_v * L->d_in * 2);
     pa.d_in = (int32_t)L->d_in;
@@ -786,6 +830,7 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
   ma.cnt = P.cnt;
   ma.part_bytes = P.part_bytes;
   ma.P = P.P;
+  ma.nst = (int32_t)(L->d_in / 64);
   // every table the kernel dereferences must be there
   if (!ma.chunks || !ma.crow || !ma.items || !ma.x || !ma.W || !ma.y ||
       (P.P > 1 && (!ma.part || !ma.cnt)) || (B->n_rot > 0 && !ma.dx) ||
@@ -793,7 +838,10 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
     return fail(SCUTE_E_STATE, "prefill path: plan tables missing");
   {
     ProfScope ps(L, st, "prefill_main");
-    hipLaunchKernelGGL(k_prefill_main<64>, dim3(P.n_items), dim3(320), 0, st, ma);
+    if (ma.nst == 64)  // d_in 4096: the K loop unrolled at compile time
+      hipLaunchKernelGGL(k_prefill_main<64>, dim3(P.n_items), dim3(320), 0, st, ma);
+    else
+      hipLaunchKernelGGL(k_prefill_main<0>, dim3(P.n_items), dim3(320), 0, st, ma);
     ++nl;
   }
   hipError_t e = hipGetLastError();

@@ -252,3 +252,29 @@ def test_deterministic_plan_is_bit_repeatable(idx, decode_mode):
     for o in outs[1:]:
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
     _check(wl, outs[0].astype(np.float64))
+
+
+def test_decode_ranks_not_multiple_of_8():
+    # ranks 4 and 12 (stored at 8 and 16 with zero rows / columns) run on the
+    # MFMA decode path
+    _need_gpu()
+    ads = [AdapterSpec("lora", rank=4), AdapterSpec("lora", rank=12, c=2.0),
+           AdapterSpec("dora", rank=12), AdapterSpec("nf", rank=4, nf_s=True, nf_term=True),
+           AdapterSpec("vera")]
+    wl = _wl(100, seed=71, adapters=ads)
+    _, y = _forward(wl, expect_path=1)
+    _check(wl, y)
+
+
+def test_decode_overflow_rows_take_the_prefill_path():
+    # 256 rows with 64 rotated rows need 10 staged row groups, more than the
+    # decode paths stage: the batch runs on the MFMA prefill path
+    _need_gpu()
+    n = 256
+    ta = np.r_[np.zeros(64, dtype=np.int64), 1 + np.arange(n - 64) % 3]
+    ads = [AdapterSpec("oft", blk=32), AdapterSpec("lora", rank=16), AdapterSpec("ia3"),
+           AdapterSpec("vera")]
+    wl = make_workload(WorkloadSpec("decode_overflow", "bf16", 512, 512, n, ads, vera_rank=64,
+                                    assign="explicit", token_adapter=ta, seed=72))
+    _, y = _forward(wl, expect_path=2)
+    _check(wl, y)

@@ -75,9 +75,15 @@ def test_fold_matches_oracle_fold(dtype):
         if own:
             t = own[0]
             r = t["A"].shape[1]
-            # A' stored [rank][d_in] = (c A diag d)^T ; B' stored [d_out][rank] = (B diag e)^T
-            _check_stored(L.read_slot(a.id, scute.SLOT_A, (r, wl.d_in), sdt), t["A"].T, dtype)
-            _check_stored(L.read_slot(a.id, scute.SLOT_B, (wl.d_out, r), sdt), t["B"].T, dtype)
+            # A' stored [rank8][d_in] = (c A diag d)^T ; B' stored [d_out][rank8] = (B diag e)^T,
+            # rank8 = r rounded up to 8 with zero padding
+            r8 = -(-r // 8) * 8
+            assert info["rank"] == r8
+            Ap = L.read_slot(a.id, scute.SLOT_A, (r8, wl.d_in), sdt)
+            Bp = L.read_slot(a.id, scute.SLOT_B, (wl.d_out, r8), sdt)
+            _check_stored(Ap[:r], t["A"].T, dtype)
+            _check_stored(Bp[:, :r], t["B"].T, dtype)
+            assert not np.any(Ap[r:]) and not np.any(Bp[:, r:])
         if fl["s"] is not None:
             _check_stored(L.read_slot(a.id, scute.SLOT_S, (wl.d_out,), np.float32), fl["s"], "f32")
         if fl["b"] is not None:
@@ -105,8 +111,9 @@ def test_dora_fold_lengths_and_e_equals_s():
     WD = oracle.dora_weight(wl.W.T, a.A.T, a.B.T, a.c, a.m)
     # s = m / colnorm(W + cAB): the folded base path W diag(s) plus the folded
     # low-rank path reproduces W_D, whose column lengths are m
-    Bp = ld.layer.read_slot(0, scute.SLOT_B, (wl.d_out, a.rank), np.float32)
-    Ap = ld.layer.read_slot(0, scute.SLOT_A, (a.rank, wl.d_in), np.float32)
+    r8 = -(-a.rank // 8) * 8  # stored rank (zero-padded to a multiple of 8)
+    Bp = ld.layer.read_slot(0, scute.SLOT_B, (wl.d_out, r8), np.float32)
+    Ap = ld.layer.read_slot(0, scute.SLOT_A, (r8, wl.d_in), np.float32)
     WD_lib = wl.W.T * s[None, :] + Ap.T @ Bp.T
     np.testing.assert_allclose(WD_lib, WD, rtol=0, atol=2e-6 * np.max(np.abs(WD)))
     np.testing.assert_allclose(np.sqrt(np.sum(WD_lib ** 2, axis=0)), a.m, rtol=2e-6)
@@ -161,7 +168,7 @@ def test_plan_stable_sort_and_classes():
     assert covered == [p for p in range(wl.n) if ta[perm[p]] >= 0]
     for (a0, s0, l0), (a1, s1, l1) in zip(seg[:-1], seg[1:]):
         assert a0 != a1 or s0 + l0 != s1
-    assert info["max_rank"] == 2
+    assert info["max_rank"] == 8  # stored ranks are padded to a multiple of 8
 
 
 def test_plan_empty_and_all_unassigned():

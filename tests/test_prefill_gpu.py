@@ -1,6 +1,7 @@
-"""GPU parity of the MFMA prefill path (bf16, d_in = 4096, d_out % 256 == 0,
-batches longer than the decode path takes) against the fp64 oracle, plus
-agreement with the generic kernels on the same inputs.
+"""GPU parity of the MFMA prefill path (bf16, d_in % 64 == 0 (% 256 with a
+rotation or a low-rank term), d_out % 256 == 0, batches the decode paths do
+not take) against the fp64 oracle, plus agreement with the generic kernels on
+the same inputs.
 
 Bars as in test_parity_gpu: max|y - ref| <= 1e-2 max|ref| and every touched
 adapter's mean effect error <= 1% of its effect.
@@ -88,8 +89,8 @@ def _segments(lengths, ids):
     return np.array(ta, dtype=np.int64)
 
 
-def _wl(name, ta, adapters=MIX, d_out=512, vera_rank=128, seed=0, **kw):
-    return make_workload(WorkloadSpec(name, "bf16", 4096, d_out, len(ta), adapters,
+def _wl(name, ta, adapters=MIX, d_out=512, vera_rank=128, seed=0, d_in=4096, **kw):
+    return make_workload(WorkloadSpec(name, "bf16", d_in, d_out, len(ta), adapters,
                                       vera_rank=vera_rank, assign="explicit", token_adapter=ta,
                                       seed=seed, **kw))
 
@@ -197,3 +198,46 @@ def test_prefill_input_scale(xscale):
     y = _forward(ld)
     _check(wl, y)
     np.testing.assert_array_equal(_forward(ld), y)
+
+
+@pytest.mark.parametrize("d_in", [5120, 2304])
+def test_prefill_other_input_widths(d_in):
+    # the K loop's stage count at run time (80 and 36 stages), K parts of the
+    # shrinks with a short last part (5 x 1024; 2 x 1024 + 256), the split
+    # into K parts of a tile where the stage count allows it
+    _need_gpu()
+    rng = np.random.default_rng(d_in)
+    ta = rng.integers(-1, len(MIX), size=600)
+    wl = _wl(f"prefill_din{d_in}", ta, seed=33, d_in=d_in, d_out=768)
+    ld = _load(wl)
+    assert ld.batch.info()["path"] == PREFILL, ld.batch.info()
+    _check(wl, _forward(ld))
+
+
+def test_prefill_input_width_multiple_of_64_without_prologue():
+    # d_in 4160 (65 stages): only slots applied in the epilogue ((IA)^3 s,
+    # a b) run on the prefill path; with a low-rank term the batch falls to
+    # the generic kernels
+    _need_gpu()
+    ads = [AdapterSpec("ia3"), AdapterSpec("nf", nf_s=True, nf_b=True)]
+    ta = np.random.default_rng(34).integers(-1, 2, size=300)
+    wl = _wl("prefill_din4160", ta, adapters=ads, seed=34, d_in=4160, d_out=512)
+    ld = _load(wl)
+    assert ld.batch.info()["path"] == PREFILL, ld.batch.info()
+    _check(wl, _forward(ld))
+    wl2 = _wl("prefill_din4160_lora", ta, adapters=[AdapterSpec("lora", rank=16)] * 2, seed=35,
+              d_in=4160, d_out=512)
+    assert _load(wl2).batch.info()["path"] == 0
+
+
+def test_prefill_ranks_not_multiple_of_8():
+    # ranks 4, 12 and 20 run on the MFMA path at the stored rank (rounded
+    # up to 8 with zero rows / columns)
+    _need_gpu()
+    ads = [AdapterSpec("lora", rank=4), AdapterSpec("lora", rank=12, c=2.0),
+           AdapterSpec("dora", rank=20), AdapterSpec("nf", rank=12, nf_s=True, nf_term=True)]
+    ta = _segments([130, 70, 200, 90, 20], [0, 1, 2, 3, -1])
+    wl = _wl("prefill_odd_ranks", ta, adapters=ads, seed=36)
+    ld = _load(wl)
+    assert ld.batch.info()["path"] == PREFILL, ld.batch.info()
+    _check(wl, _forward(ld))
