@@ -167,24 +167,35 @@ def matched_lora(wl):
 
 
 def cpu_baseline(wl, seconds):
-    import numpy as np
+    """The oracle on the host cores: three timed runs of whole batches of the
+    same workload (each at least seconds / 3), reporting the median rate."""
+    import statistics
+    import numpy as np  # noqa: F401
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:
         cores = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.forward(wl)
-        reps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": wl.n * reps / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"whole batch ({wl.n} tokens) of the same workload, {reps} repetition(s), "
-                      f"{dt:.1f} s of numpy fp64 on {cores} BLAS thread(s)"}
+    rates, reps_all, dt_all = [], 0, 0.0
+    for _ in range(3):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.forward(wl)
+            reps += 1
+            if time.perf_counter() - t0 >= seconds / 3:
+                break
+        dt = time.perf_counter() - t0
+        rates.append(wl.n * reps / dt)
+        reps_all += reps
+        dt_all += dt
+    return {"value": statistics.median(rates), "unit": "tokens/s", "cores": int(cores),
+            "host_cpu_count": os.cpu_count(), "kind": "oracle",
+            "sample": f"median of 3 runs of whole batches ({wl.n} tokens) of the same workload, "
+                      f"{reps_all} repetition(s) in {dt_all:.1f} s of numpy fp64 on {cores} BLAS "
+                      f"thread(s) (host reports {os.cpu_count()} CPUs)",
+            "runs": [round(r, 3) for r in rates]}
 
 
 def measure(torch, wl, steps, warmup):

@@ -3,6 +3,12 @@
 Every HIP source is compiled with packed-fp32 instructions disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); host sources are
 plain C++17 compiled by hipcc's host pass.
+
+``build(sanitize=True)`` (``python -m lora_normal_form_amd.build --sanitize``)
+builds libscute_san.so instead: the host side of every source with
+AddressSanitizer and UndefinedBehaviorSanitizer (``-Xarch_host`` in front of
+each ``-fsanitize=``, so no device code is instrumented), for host-only runs
+(``python -m lora_normal_form_amd.sanitize_check``).
 """
 
 from __future__ import annotations
@@ -17,6 +23,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libscute.so")
+BUILD_SAN = os.path.join(PKG, "_build_san")
+LIB_SAN = os.path.join(PKG, "libscute_san.so")
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address",
+             "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=undefined"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -37,14 +47,16 @@ def _run(cmd):
     return r.stdout
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every source and link libscute.so. Returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    """Compile every source and link libscute.so (libscute_san.so with
+    sanitize). Returns the library path."""
+    bdir, lib = (BUILD_SAN, LIB_SAN) if sanitize else (BUILD, LIB)
+    os.makedirs(bdir, exist_ok=True)
     t0 = time.time()
     cmds, objs = [], []
     for src in HOST_SRCS + HIP_SRCS:
-        obj = os.path.join(BUILD, src + ".o")
-        flags = COMMON + (HIP_FLAGS if src.endswith(".hip") else [])
+        obj = os.path.join(bdir, src + ".o")
+        flags = COMMON + (HIP_FLAGS if src.endswith(".hip") else []) + (SAN_FLAGS if sanitize else [])
         cmds.append([HIPCC] + flags + ["-c", "-o", obj, os.path.join(CSRC, src)])
         objs.append(obj)
     procs = []
@@ -63,13 +75,15 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             sys.stderr.write(out)
     if failed:
         raise RuntimeError("libscute build failed")
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+    tmp = lib + ".tmp"
+    link = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-shared-libasan"] if sanitize else []
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + link + objs)
+    os.replace(tmp, lib)
     if verbose:
-        sys.stderr.write(f"built {LIB} in {time.time() - t0:.1f}s\n")
-    return LIB
+        sys.stderr.write(f"built {lib} in {time.time() - t0:.1f}s\n")
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, sanitize="--sanitize" in sys.argv[1:]))

@@ -17,7 +17,8 @@ from typing import Dict, Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libscute.so")
+# SCUTE_LIB names another build of the library (the sanitized host build)
+LIB_PATH = os.environ.get("SCUTE_LIB") or os.path.join(_HERE, "libscute.so")
 
 OK = 0
 E_INVALID, E_SHAPE, E_NOMEM, E_HIP, E_STATE, E_UNSUPPORTED = -1, -2, -3, -4, -5, -6

@@ -39,3 +39,14 @@ def test_counter_sources_hash_ignores_comments_only():
     # literals that look like comments stay, and a change of code is seen
     assert '"x // y /* z */"' in strip_comments(code)
     assert strip_comments(code) != strip_comments(code.replace("a = 1", "a = 2"))
+
+
+def test_cpu_baseline_is_median_of_three_runs():
+    import bench
+    from synth import make_config
+    wl = make_config(0)
+    cb = bench.cpu_baseline(wl, 0.3)
+    assert cb["kind"] == "oracle" and cb["unit"] == "tokens/s"
+    assert len(cb["runs"]) == 3
+    assert cb["value"] == sorted(cb["runs"])[1] or abs(cb["value"] - sorted(cb["runs"])[1]) < 1e-3
+    assert cb["cores"] >= 1 and cb["host_cpu_count"] == __import__("os").cpu_count()

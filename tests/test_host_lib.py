@@ -319,3 +319,14 @@ def test_route_extra_bytes_by_hand():
     assert costmodel.route_extra("rotate_pass", n=128, d_out=4096, rot_rows=26) == (0.0, 1)
     with pytest.raises(ValueError):
         costmodel.route_extra("nope", n=1, d_out=1)
+
+
+def test_sanitizer_build_instruments_host_code_only():
+    # every -fsanitize= of the sanitized build follows -Xarch_host, so hipcc
+    # instruments only the host side (no sanitized device code)
+    from lora_normal_form_amd import build as B
+    for flags in (B.SAN_FLAGS,):
+        for i, f in enumerate(flags):
+            if f.startswith("-fsanitize") or f.startswith("-fno-sanitize"):
+                assert i > 0 and flags[i - 1] == "-Xarch_host", flags
+    assert B.LIB_SAN != B.LIB and B.BUILD_SAN != B.BUILD
