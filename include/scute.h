@@ -269,6 +269,17 @@ scute_status scute_layer_forward_noalloc(scute_layer* layer, const int32_t* toke
                                          int32_t n, const void* x, const void* W, float* y,
                                          void* stream);
 
+/* The FFN gate after the up projection: h = silu(g) (.) u element-wise, with
+ * silu(z) = z / (1 + exp(-z)), the gate activation of the Llama models the
+ * pages evaluate on. (IA)^3 multiplies the FFN intermediate
+ * sigma(x W_g) (.) (x W_u) by l; products reorder, so l is the s slot of the
+ * up projection ("The big picture: six extra slots in the LoRA
+ * computation"), u is that layer's output and g the gate projection's.
+ * g, u, h: DEVICE float32 arrays of `count` elements, h may be u; 16-byte
+ * aligned. Errors: SCUTE_E_INVALID for null or misaligned pointers or
+ * count < 0; SCUTE_E_HIP if the launch fails. */
+scute_status scute_silu_gate(const float* g, const float* u, float* h, int64_t count, void* stream);
+
 /* Algorithmic bytes / FLOPs / launches of one forward with this plan. */
 scute_status scute_cost_model(const scute_layer* layer, const scute_batch* batch,
                               scute_cost* out);

@@ -20,6 +20,7 @@
 
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "internal.h"
@@ -360,7 +361,42 @@ extern "C" scute_status scute_layer_forward(scute_layer* L, const scute_batch* B
 
 namespace scute {
 __global__ void k_empty() {}
+
+// h = silu(g) (.) u, four elements per thread and grid-stride rounds
+__global__ void __launch_bounds__(256) k_silu_gate(const float* __restrict__ g, const float* __restrict__ u,
+                                                   float* h, int64_t count) {
+  const int64_t n4 = count / 4;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    const float4 gv = reinterpret_cast<const float4*>(g)[i];
+    const float4 uv = reinterpret_cast<const float4*>(u)[i];
+    float4 o;
+    o.x = gv.x / (1.f + expf(-gv.x)) * uv.x;
+    o.y = gv.y / (1.f + expf(-gv.y)) * uv.y;
+    o.z = gv.z / (1.f + expf(-gv.z)) * uv.z;
+    o.w = gv.w / (1.f + expf(-gv.w)) * uv.w;
+    reinterpret_cast<float4*>(h)[i] = o;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < count - 4 * n4) {
+    const int64_t i = 4 * n4 + threadIdx.x;
+    h[i] = g[i] / (1.f + expf(-g[i])) * u[i];
+  }
+}
 }  // namespace scute
+
+extern "C" scute_status scute_silu_gate(const float* g, const float* u, float* h, int64_t count, void* stream) {
+  using namespace scute;
+  if (count < 0) return fail(SCUTE_E_INVALID, "scute_silu_gate: count must be >= 0");
+  if (count == 0) return SCUTE_OK;
+  if (!g || !u || !h) return fail(SCUTE_E_INVALID, "scute_silu_gate: null pointer");
+  if (((uintptr_t)g | (uintptr_t)u | (uintptr_t)h) & 15)
+    return fail(SCUTE_E_INVALID, "scute_silu_gate: g, u and h must be 16-byte aligned");
+  const int64_t blocks = std::min<int64_t>(std::max<int64_t>(1, (count / 4 + 255) / 256), 8192);
+  hipLaunchKernelGGL(k_silu_gate, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, g, u, h, count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "scute_silu_gate");
+  return SCUTE_OK;
+}
 
 extern "C" scute_status scute_launch_empty(int32_t count, void* stream) {
   using namespace scute;

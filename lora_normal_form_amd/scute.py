@@ -93,6 +93,7 @@ SIGNATURES = {
     "scute_profile_read": (C.c_int32, [_P, C.POINTER(KernelTime), C.c_int32,
                                        C.POINTER(C.c_int32)]),
     "scute_launch_empty": (C.c_int32, [C.c_int32, _P]),
+    "scute_silu_gate": (C.c_int32, [_P, _P, _P, C.c_int64, _P]),
     "scute_last_error": (C.c_char_p, []),
     "scute_version": (C.c_char_p, []),
 }
@@ -199,6 +200,12 @@ def scute_plan_batch_flags(layer: int, token_adapter, flags: int, stream=None) -
     _check(lib.scute_plan_batch_flags(layer, ta.ctypes.data if ta.size else None, int(ta.size),
                                       int(flags), _stream_ptr(stream), C.byref(h)))
     return h.value
+
+
+def scute_silu_gate(g, u, h, count=None, stream=None) -> None:
+    """h = silu(g) (.) u on device float32 tensors."""
+    n = int(h.numel() if count is None else count)
+    _check(lib.scute_silu_gate(_ptr(g), _ptr(u), _ptr(h), n, _stream_ptr(stream)))
 
 
 def scute_launch_empty(count: int, stream=None) -> None:
