@@ -34,7 +34,7 @@
 //            gives the same bits.
 //   meet     every slice stores its raw partial piece (row group g, wave w:
 //            32 rows x 32 outputs) and counts its arrival; one slice per
-//            piece (slice g S / MG: the pieces spread over the slices) waits
+//            piece (slice g % S: the pieces dealt round the slices) waits
 //            for all of them, adds the slices' pieces in slice order and
 //            finishes it: (.) s, the own low-rank expand t B' (not scaled by
 //            s: s multiplies the base output only), the shared VeRA product
@@ -254,11 +254,12 @@ __device__ __forceinline__ uint32_t piece_part(uint32_t base, int q, int lane) {
 
 constexpr int FD_LDS_STEPS = 256;  // expand-step descriptors kept in LDS
 
-// Slice finishing piece (g, w) of a tile: the groups are spread over the
-// slices (group g to slice g S / MG), so with MG <= S each wave finishes at
-// most one piece. Accumulator element i: row 32 g + m, output
-// f0 + 8 (i / 4) + 4 h + i % 4.
-__device__ __forceinline__ int fd_reducer(int g, int S, int MG) { return g * S / MG; }
+// Slice finishing piece (g, w) of a tile: the groups are dealt round the
+// slices (group g to slice g % S), so with MG <= S each wave finishes at most
+// one piece and with MG > S neighbouring groups (VeRA rows and the rest come
+// in runs of groups) land on different slices. Accumulator element i: row
+// 32 g + m, output f0 + 8 (i / 4) + 4 h + i % 4.
+__device__ __forceinline__ int fd_reducer(int g, int S) { return g % S; }
 
 constexpr int FD_TJ = 4;  // own shrink sums a lane holds (ranks up to 64 in 16-rank steps)
 
@@ -645,7 +646,7 @@ __global__ void __launch_bounds__(256, 1) k_fd_main(FdArgs a) {
   if (!live) return;
 #pragma unroll
   for (int g = 0; g < MGT; ++g)
-    if (g < MG && fd_reducer(g, a.S, MG) == k)
+    if (g < MG && fd_reducer(g, a.S) == k)
       fd_finish_piece<MGT <= 5 ? 8 : 4>(a, rec[32 * g + m], acc[g], g, k, f0, lane, m, h, pr,
                       tile_base + (uint32_t)(g * FWAVES + w) * 4096u, piece_stride,
                       a.cnt + (c * MG + g) * FWAVES + w, sst);

@@ -18,6 +18,8 @@
 // This file holds the generic kernels: correct for every shape the ABI
 // accepts, in fp32 or bf16, with fp32 accumulation.
 
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -323,14 +325,40 @@ int32_t forward_launch_count(const scute_layer* L, const scute_batch* B) {
          (B->max_rank > 0 || B->n_vera > 0);
 }
 
-scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x, const void* W,
-                            float* y, hipStream_t st, int32_t* launches) {
+// SCUTE_TRACE=1 in the environment (read once): one line per forward on
+// stderr with the path, the batch's shape and the launches it made
+static bool trace_on() {
+  static const bool on = [] {
+    const char* v = getenv("SCUTE_TRACE");
+    return v && *v && *v != '0';
+  }();
+  return on;
+}
+
+static scute_status launch_path(scute_layer* L, const scute_batch* B, const void* x, const void* W, float* y,
+                                hipStream_t st, int32_t* launches) {
   if (B->fp.enabled) return launch_fdecode(L, B, x, W, y, st, launches);
   if (B->dp.enabled) return launch_decode(L, B, x, W, y, st, launches);
   if (B->pp.enabled) return launch_prefill(L, B, x, W, y, st, launches);
   if (L->act == SCUTE_BF16)
     return launch_ref<uint16_t>(L, B, (const uint16_t*)x, (const uint16_t*)W, y, st, launches);
   return launch_ref<float>(L, B, (const float*)x, (const float*)W, y, st, launches);
+}
+
+scute_status launch_forward(scute_layer* L, const scute_batch* B, const void* x, const void* W,
+                            float* y, hipStream_t st, int32_t* launches) {
+  int32_t nl = 0;
+  const scute_status s = launch_path(L, B, x, W, y, st, &nl);
+  if (launches) *launches = nl;
+  if (trace_on()) {
+    const char* path = B->fp.enabled ? "fused-decode" : B->dp.enabled ? "decode" : B->pp.enabled ? "prefill" : "generic";
+    fprintf(stderr,
+            "scute: forward layer=%p plan=%p path=%s n=%d d_in=%lld d_out=%lld segments=%d rot_rows=%d "
+            "vera_rows=%d max_rank=%d route=0x%x launches=%d status=%d\n",
+            (const void*)L, (const void*)B, path, B->n, (long long)L->d_in, (long long)L->d_out, B->nseg(),
+            B->n_rot, B->n_vera, B->max_rank, B->dp.route, nl, (int)s);
+  }
+  return s;
 }
 
 }  // namespace scute

@@ -146,11 +146,43 @@ def traffic(fetch_csv: str, write_csv: str, copy_mib: float, workload: str) -> d
             "fetch_scale": f_scale, "write_scale": w_scale, "kernels": kernels}
 
 
+def mfma_table(path: str, simds: int = 1024, xcds: int = 8) -> str:
+    """MFMA use per kernel from one counter run of SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16 (medians over the
+    dispatches). GRBM_GUI_ACTIVE comes summed over the XCDs, so the busy
+    fraction is MFMA-busy SIMD cycles / (GPU-active cycles / XCDs x SIMDs,
+    4 per CU); the MOPS counter counts 512 flops, and the achieved rate
+    divides them by the dispatch's own start-to-end time in the counter run."""
+    per = defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        d = per[key]
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    by_kernel = defaultdict(list)
+    for (name, _), d in per.items():
+        k = short_name(name)
+        if k is None or "GRBM_GUI_ACTIVE" not in d or d["GRBM_GUI_ACTIVE"] <= 0:
+            continue
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (d["GRBM_GUI_ACTIVE"] / xcds * simds)
+        flops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        by_kernel[k].append((busy, flops, flops / max(1, d["ns"]) / 1e3))
+    out = ["| kernel | dispatches | MFMA busy (% of SIMD cycles) | bf16 MFMA GFLOP per dispatch | "
+           "TFLOP/s in the counter run |", "|---|---|---|---|---|"]
+    for k in sorted(by_kernel):
+        v = by_kernel[k]
+        med = lambda i: sorted(x[i] for x in v)[len(v) // 2]  # noqa: E731
+        out.append(f"| `{k}` | {len(v)} | {100 * med(0):.1f} | {med(1) / 1e9:.2f} | {med(2):.0f} |")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("csv")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -160,6 +192,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv))
+    elif a.cmd == "mfma":
+        print(mfma_table(a.csv))
     else:
         res = traffic(a.fetch, a.write, a.copy_mib, a.workload)
         with open(a.out, "w") as f:

@@ -214,3 +214,24 @@ def test_plan_freed_after_its_layer():
     t.fill_(1.0)
     torch.cuda.synchronize()
     assert float(t.sum()) == 1024.0
+
+
+def test_trace_logs_one_line_per_forward():
+    # SCUTE_TRACE=1 (read once per process): the path, shape and launch count
+    # of every forward on stderr; run in a child process so the setting is
+    # fresh
+    _need_gpu()
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import torch\nfrom synth import make_config\nfrom lora_normal_form_amd import workload as glue\n"
+            "wl = make_config(0)\nld = glue.load(wl, device=0)\n"
+            "for _ in range(2):\n    ld.layer.forward(ld.batch, ld.x, ld.W, ld.y)\n"
+            "torch.cuda.synchronize()\n")
+    env = dict(os.environ, SCUTE_TRACE="1", PYTHONPATH=root)
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("scute: forward")]
+    assert len(lines) == 2, r.stderr[-2000:]
+    assert "path=generic" in lines[0] and "n=16" in lines[0] and "status=0" in lines[0]
