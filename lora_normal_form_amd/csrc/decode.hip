@@ -955,16 +955,16 @@ k_decode_main(MainArgs a) {
 // launcher
 // ---------------------------------------------------------------------------
 
-void launch_prologue(const ProArgs& pa, int grid, hipStream_t st) {
-  hipLaunchKernelGGL(k_decode_prologue, dim3(grid), dim3(64), 0, st, pa);
+void launch_prologue(const ProArgs& pa, int grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  hipExtLaunchKernelGGL(k_decode_prologue, dim3(grid), dim3(64), 0, st, e0, e1, 0, pa);
 }
 
 template <int MGT>
-static void launch_main(const MainArgs& a, dim3 grid, hipStream_t st) {
+static void launch_main(const MainArgs& a, dim3 grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (a.k_chunk / 2 / SK) {
-    case 8: hipLaunchKernelGGL((k_decode_main<MGT, 8>), dim3(grid), dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((k_decode_main<MGT, 32>), dim3(grid), dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_decode_main<MGT, 0>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipExtLaunchKernelGGL((k_decode_main<MGT, 8>), grid, dim3(256), 0, st, e0, e1, 0, a); break;
+    case 32: hipExtLaunchKernelGGL((k_decode_main<MGT, 32>), grid, dim3(256), 0, st, e0, e1, 0, a); break;
+    default: hipExtLaunchKernelGGL((k_decode_main<MGT, 0>), grid, dim3(256), 0, st, e0, e1, 0, a); break;
   }
 }
 
@@ -998,8 +998,8 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
     pa.RT = D.RT;
     pa.d_in = (int32_t)L->d_in;
     const int grid = std::max(1, std::min(8192, pa.n_items));
-    ProfScope ps(L, st, "decode_prologue");
-    launch_prologue(pa, grid, st);
+    ProfScope ps(L, st, "decode_prologue", true);
+    launch_prologue(pa, grid, st, ps.ev_start(), ps.ev_stop());
     ++nl;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch k_decode_prologue");
@@ -1033,16 +1033,16 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.gv1 = D.gv1;
   ma.r_v = L->r_v;
   const dim3 grid(D.C, D.S);
-  ProfScope ps(L, st, "decode_main");
+  ProfScope ps(L, st, "decode_main", true);
   switch (D.MG + D.g_rot) {
-    case 1: launch_main<1>(ma, grid, st); break;
-    case 3: launch_main<3>(ma, grid, st); break;
-    case 4: launch_main<4>(ma, grid, st); break;
-    case 5: launch_main<5>(ma, grid, st); break;
-    case 6: launch_main<6>(ma, grid, st); break;
-    case 7: launch_main<7>(ma, grid, st); break;
-    case 8: launch_main<8>(ma, grid, st); break;
-    case 9: launch_main<9>(ma, grid, st); break;
+    case 1: launch_main<1>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
+    case 3: launch_main<3>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
+    case 4: launch_main<4>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
+    case 5: launch_main<5>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
+    case 6: launch_main<6>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
+    case 7: launch_main<7>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
+    case 8: launch_main<8>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
+    case 9: launch_main<9>(ma, grid, st, ps.ev_start(), ps.ev_stop()); break;
     default: return fail(SCUTE_E_UNSUPPORTED, "decode path: unsupported staged row groups");
   }
   ++nl;

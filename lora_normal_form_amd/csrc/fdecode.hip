@@ -653,12 +653,12 @@ __global__ void __launch_bounds__(256, 1) k_fd_main(FdArgs a) {
 }
 
 template <int MGT>
-void launch_fd_main(const FdArgs& a, int grid, int nst, hipStream_t st) {
+void launch_fd_main(const FdArgs& a, int grid, int nst, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (nst) {
-    case 8: hipLaunchKernelGGL((k_fd_main<MGT, 8>), dim3(grid), dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((k_fd_main<MGT, 16>), dim3(grid), dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((k_fd_main<MGT, 32>), dim3(grid), dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_fd_main<MGT, 0>), dim3(grid), dim3(256), 0, st, a); break;
+    case 8: hipExtLaunchKernelGGL((k_fd_main<MGT, 8>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a); break;
+    case 16: hipExtLaunchKernelGGL((k_fd_main<MGT, 16>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a); break;
+    case 32: hipExtLaunchKernelGGL((k_fd_main<MGT, 32>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a); break;
+    default: hipExtLaunchKernelGGL((k_fd_main<MGT, 0>), dim3(grid), dim3(256), 0, st, e0, e1, 0, a); break;
   }
 }
 
@@ -721,16 +721,16 @@ scute_status launch_fdecode(scute_layer* L, const scute_batch* B, const void* x,
     return fail(SCUTE_E_STATE, "fused decode: plan tables missing");
   const int grid = P.CG * P.S;
   {
-    ProfScope ps(L, st, "fd_main");
+    ProfScope ps(L, st, "fd_main", true);
     switch (P.MGT) {
-      case 1: launch_fd_main<1>(a, grid, P.NST, st); break;
-      case 2: launch_fd_main<2>(a, grid, P.NST, st); break;
-      case 3: launch_fd_main<3>(a, grid, P.NST, st); break;
-      case 4: launch_fd_main<4>(a, grid, P.NST, st); break;
-      case 5: launch_fd_main<5>(a, grid, P.NST, st); break;
-      case 6: launch_fd_main<6>(a, grid, P.NST, st); break;
-      case 7: launch_fd_main<7>(a, grid, P.NST, st); break;
-      case 8: launch_fd_main<8>(a, grid, P.NST, st); break;
+      case 1: launch_fd_main<1>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
+      case 2: launch_fd_main<2>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
+      case 3: launch_fd_main<3>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
+      case 4: launch_fd_main<4>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
+      case 5: launch_fd_main<5>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
+      case 6: launch_fd_main<6>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
+      case 7: launch_fd_main<7>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
+      case 8: launch_fd_main<8>(a, grid, P.NST, st, ps.ev_start(), ps.ev_stop()); break;
       default: return fail(SCUTE_E_UNSUPPORTED, "fused decode: unsupported staged row groups");
     }
     ++nl;

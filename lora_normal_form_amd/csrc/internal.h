@@ -1,6 +1,7 @@
 // Internal definitions shared by the host runtime and the HIP kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -432,16 +433,20 @@ struct ProArgs {
   int32_t M_pad, AW, RT;
   int32_t d_in;
 };
-void launch_prologue(const ProArgs& pa, int grid, hipStream_t st);
+void launch_prologue(const ProArgs& pa, int grid, hipStream_t st, hipEvent_t e0, hipEvent_t e1);
 
 // Kernel timing: when the layer has profiling on, bracket each launch with a
 // HIP event pair on the launch stream.
+// in_launch: the launch records the pair itself (hipExtLaunchKernelGGL with
+// ev_start() / ev_stop()), so the pair times the kernel's execution, as a
+// kernel trace does, without the dispatch around it.
 struct ProfScope {
   scute_layer* L;
   hipStream_t st;
   ProfEvent ev{};
-  bool on = false;
-  ProfScope(scute_layer* L_, hipStream_t st_, const char* name) : L(L_), st(st_) {
+  bool on = false, in_launch = false;
+  ProfScope(scute_layer* L_, hipStream_t st_, const char* name, bool in_launch_ = false)
+      : L(L_), st(st_), in_launch(in_launch_) {
     if (!L->profiling) return;
     int32_t kind = -1;
     for (size_t i = 0; i < L->prof_names.size(); ++i)
@@ -461,11 +466,13 @@ struct ProfScope {
         return;
       }
     }
-    on = hipEventRecord(ev.start, st) == hipSuccess;
+    on = in_launch || hipEventRecord(ev.start, st) == hipSuccess;
   }
+  hipEvent_t ev_start() const { return on ? ev.start : nullptr; }
+  hipEvent_t ev_stop() const { return on ? ev.stop : nullptr; }
   ~ProfScope() {
     if (!on) return;
-    if (hipEventRecord(ev.stop, st) == hipSuccess) L->prof_pending.push_back(ev);
+    if (in_launch || hipEventRecord(ev.stop, st) == hipSuccess) L->prof_pending.push_back(ev);
   }
 };
 

@@ -802,8 +802,9 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
     pa.AW = P.AW;
     pa.RT = P.RT;
     pa.r_v = L->r_v;
-    ProfScope ps(L, st, "prefill_prologue");
-    hipLaunchKernelGGL(k_prefill_prologue, dim3(P.n_pro), dim3(256), 0, st, pa);
+    ProfScope ps(L, st, "prefill_prologue", true);
+    hipExtLaunchKernelGGL(k_prefill_prologue, dim3(P.n_pro), dim3(256), 0, st, ps.ev_start(), ps.ev_stop(),
+                          0, pa);
     ++nl;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch k_prefill_prologue");
@@ -837,11 +838,13 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
       (B->n_vera > 0 && !ma.B_sh) || (P.AW > 0 && !ma.tbf))
     return fail(SCUTE_E_STATE, "prefill path: plan tables missing");
   {
-    ProfScope ps(L, st, "prefill_main");
+    ProfScope ps(L, st, "prefill_main", true);
     if (ma.nst == 64)  // d_in 4096: the K loop unrolled at compile time
-      hipLaunchKernelGGL(k_prefill_main<64>, dim3(P.n_items), dim3(320), 0, st, ma);
+      hipExtLaunchKernelGGL(k_prefill_main<64>, dim3(P.n_items), dim3(320), 0, st, ps.ev_start(),
+                            ps.ev_stop(), 0, ma);
     else
-      hipLaunchKernelGGL(k_prefill_main<0>, dim3(P.n_items), dim3(320), 0, st, ma);
+      hipExtLaunchKernelGGL(k_prefill_main<0>, dim3(P.n_items), dim3(320), 0, st, ps.ev_start(),
+                            ps.ev_stop(), 0, ma);
     ++nl;
   }
   hipError_t e = hipGetLastError();
