@@ -39,3 +39,13 @@ def test_checker_flags_a_w_load_moved_above_a_row_load():
                     reason="hipcc not installed")
 def test_compiled_kernel_keeps_the_issue_order():
     assert issue_order.main() == 0
+
+
+def test_phase_stamps_apply_to_the_decode_kernel():
+    # the phase-timestamp tool instruments k_decode_main at fixed anchors;
+    # every anchor must still be found exactly once
+    from lora_normal_form_amd import phases
+    src = open(os.path.join(build.CSRC, "decode.hip")).read()
+    out = phases._patch(src)
+    assert out.count("phase_stamp(") == 9  # the helper plus eight boundaries
+    assert "scute_phase_read" in out
