@@ -26,6 +26,7 @@ import json
 import math
 import os
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -208,7 +209,22 @@ def measure(torch, wl, steps, warmup):
     gpu_ms, wall, _ = time_forwards(torch, sets, steps, warmup)
     _, _, kernels = time_forwards(torch, sets, steps, warmup, profile=True)
     return {"cost": cost, "n_sets": n_sets, "gpu_ms": gpu_ms, "wall": wall, "kernels": kernels,
-            "sets": sets}
+            "sets": sets, "plan_us": plan_host_us(torch, first[0], wl)}
+
+
+def plan_host_us(torch, ld, wl, reps=20):
+    """Host time of building the batch plan (segment builder and its tables'
+    upload), median of `reps` builds; the plan is built once, outside the
+    timed loop."""
+    ts = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        b = ld.layer.plan(wl.token_adapter)
+        torch.cuda.synchronize()
+        ts.append((time.perf_counter() - t0) * 1e6)
+        b.close()
+    return round(statistics.median(ts), 1)
 
 
 def main():
@@ -265,7 +281,8 @@ def main():
              "flops_per_forward": cost["flops"], "launches_per_forward": cost["launches"],
              "kernels_us": {k: round(v["total_ms"] / max(1, v["launches"]) * 1e3, 3)
                             for k, v in kern.items()},
-             "rotating_sets": m["n_sets"], "wall_s": round(m["wall"], 4)}
+             "rotating_sets": m["n_sets"], "wall_s": round(m["wall"], 4),
+             "plan_host_us": m["plan_us"]}
     del m
 
     if not args.no_overhead and args.workload == 2:
