@@ -138,6 +138,35 @@ def test_decode_path_split_k(splitk):
     _check(wl, y)
 
 
+@pytest.mark.parametrize("case", ["d_in_8192", "r_v_32", "r_v_96_dense", "r_v_96_steps", "oft_blk4",
+                                  "oft_blk8", "oft_blk16"])
+def test_decode_edge_shapes(case, decode_mode):
+    # the largest d_in the decode paths take (16 pieces per lane in the
+    # gather), VeRA pairs whose rank is not a multiple of 64 (dense product
+    # forced on and off), and rotation blocks below 32 (the rotation's
+    # 8-wide and scalar branches)
+    _need_gpu()
+    ads = MIX
+    kw = dict(d_in=512, d_out=384, vera_rank=64)
+    env = {}
+    if case == "d_in_8192":
+        kw.update(d_in=8192, d_out=512)
+    elif case == "r_v_32":
+        kw.update(vera_rank=32)
+    elif case.startswith("r_v_96"):
+        kw.update(vera_rank=96)
+        ads = [AdapterSpec("vera"), AdapterSpec("vera", bias=True), AdapterSpec("lora", rank=8),
+               AdapterSpec("ia3")]
+        env["SCUTE_DECODE_DENSE_VERA"] = 1 if case.endswith("dense") else 0
+    else:
+        blk = int(case[len("oft_blk"):])
+        ads = [AdapterSpec("oft", blk=blk), AdapterSpec("lora", rank=16), AdapterSpec("vera"),
+               AdapterSpec("oft", blk=blk, bias=True)]
+    wl = _wl(120, seed=400 + len(case), adapters=ads, **kw)
+    _, y = _forward(wl, expect_path=1, **env)
+    _check(wl, y)
+
+
 def test_decode_matches_generic_kernels():
     _need_gpu()
     wl = _wl(150, seed=12)
