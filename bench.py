@@ -117,7 +117,8 @@ def dominant_kernel_bytes(name, wl, cost):
 
     decode_main (base GEMM + fused expand): x, W, y, touched adapters' B', s,
     b, VeRA e, and the shared B_sh once; decode_prologue (rotation, shrinks):
-    x, A', P, VeRA d, shared A_sh; generic gemm: x, W, y.
+    x, A', P, VeRA d, shared A_sh; fd_main (the fused decode kernel): all of
+    the forward's bytes but the rotation blocks; generic gemm: x, W, y.
     """
     es = 2 if wl.dtype == "bf16" else 4
     xwy = wl.n * wl.d_in * es + wl.d_in * wl.d_out * es + wl.n * wl.d_out * 4
@@ -125,9 +126,26 @@ def dominant_kernel_bytes(name, wl, cost):
         return cost["gemm_bytes"]
     if name == "decode_prologue":
         return cost["prologue_bytes"]
+    if name == "fd_main":
+        # the fused kernel moves everything but the rotation blocks, which
+        # fd_rotate reads: x, W, y, touched adapters' factors and vectors,
+        # the shared VeRA pair
+        return cost["bytes"] - rotation_bytes(wl)
     if name == "gemm":
         return xwy
     return None
+
+
+def rotation_bytes(wl):
+    """Stored rotation blocks (R - I) of the adapters that have tokens: d_in x
+    blk elements each, at the activation size."""
+    es = 2 if wl.dtype == "bf16" else 4
+    touched = set(int(a) for a in wl.token_adapter if a >= 0)
+    total = 0
+    for a in wl.adapters:
+        if a.id in touched and (a.Q is not None or a.R is not None):
+            total += wl.d_in * a.blk * es
+    return total
 
 
 def measured_traffic(kernel, wl):

@@ -385,8 +385,17 @@ int32_t forward_launch_count(const scute_layer* L, const scute_batch* B);
 
 // Decode path selection (environment SCUTE_DECODE, read when a batch is
 // planned): 0 = generic kernels only, 1 = the fused single-kernel path
-// (fdecode.hip), 2 = the two-launch path (decode.hip); unset = DECODE_DEFAULT.
+// (fdecode.hip), 2 = the two-launch path (decode.hip). Unset: the fused path
+// for batches of at least FUSED_MIN_GROUPS staged row groups in which no row
+// has an own low-rank term, the two-launch path (DECODE_DEFAULT) otherwise.
+// Measured on MI355X: with 7 or more row groups the two-launch kernel keeps
+// only a 2-slot ring of 64-column tiles, while the fused kernel's
+// 128-column tiles feed four column blocks from each staged row; the fused
+// kernel's extra work is its in-loop shrink blocks, which own terms add per
+// adapter (256 (IA)^3 / VeRA rows: 86 against 91 us at 4096 -> 14336, 73
+// against 91 us at 11008; 256 LoRA rows: 95 against 83 us).
 constexpr int DECODE_DEFAULT = 2;
+constexpr int FUSED_MIN_GROUPS = 7;
 
 // decode path (decode.hip / plan.cpp)
 scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t st);

@@ -42,8 +42,10 @@ scute_status build_fdecode_plan(const scute_layer* L, scute_batch* B, hipStream_
   const int64_t d_in = L->d_in, d_out = L->d_out;
   // the fused path: SCUTE_DECODE=1, or any decode path mode (not 0) when the
   // plan asks for bit-repeatable forwards
-  const int mode = env_int("SCUTE_DECODE", DECODE_DEFAULT);
-  if (mode == 0 || (mode != 1 && !(B->flags & SCUTE_PLAN_DETERMINISTIC))) return SCUTE_OK;
+  // (SCUTE_DECODE unset: -1, the choice below)
+  const int mode = env_int("SCUTE_DECODE", -1);
+  const bool det = (B->flags & SCUTE_PLAN_DETERMINISTIC) != 0;
+  if (mode == 0 || (mode != 1 && mode != -1 && !det)) return SCUTE_OK;
   if (L->act != SCUTE_BF16 || n <= 0 || n > 256) return SCUTE_OK;
   if (d_in % 64 != 0 || d_out % 32 != 0) return SCUTE_OK;
   // W, x and every workspace are addressed through buffer ranges with
@@ -58,6 +60,16 @@ scute_status build_fdecode_plan(const scute_layer* L, scute_batch* B, hipStream_
   F.g_rot = (B->n_rot + 31) / 32;
   F.MGT = F.MG + F.g_rot;
   if (F.MGT > 8) return SCUTE_OK;
+  if (mode == -1 && !det) {
+    // path unset: the fused path only for many staged row groups and no own
+    // low-rank term (see FUSED_MIN_GROUPS)
+    bool own = false;
+    for (int32_t i = 0; i < B->nseg(); ++i) own |= (L->table[B->seg[3 * i]].flags & F_TERM) != 0;
+    if (own || F.MGT < FUSED_MIN_GROUPS) {
+      F = FdPlan{};
+      return SCUTE_OK;
+    }
+  }
   F.M_pad = 32 * F.MG;
   F.RT = (B->max_rank + 15) / 16 * 16;
   F.AW = F.RT + (B->n_vera > 0 ? L->r_v : 0);

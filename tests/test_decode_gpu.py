@@ -167,6 +167,38 @@ def test_decode_edge_shapes(case, decode_mode):
     _check(wl, y)
 
 
+@pytest.mark.parametrize("kind", ["ia3_vera_256", "lora_256", "ia3_vera_128"])
+def test_decode_path_choice_when_unset(kind, decode_mode):
+    # with SCUTE_DECODE unset the planner takes the fused path for batches of
+    # 7 or more staged row groups with no own low-rank term, the two-launch
+    # path otherwise; the kernels a forward runs show which
+    if decode_mode != 2:
+        pytest.skip("one run per case: the choice does not depend on the fixture's mode")
+    _need_gpu()
+    from lora_normal_form_amd import scute
+    n = 128 if kind.endswith("128") else 256
+    ads = ([AdapterSpec("ia3"), AdapterSpec("vera")] * 4 if kind.startswith("ia3")
+           else [AdapterSpec("lora", rank=16)] * 8)
+    wl = _wl(n, seed=500 + n, adapters=ads, none_frac=0.0, d_in=1024, d_out=512)
+    saved = os.environ.pop("SCUTE_DECODE", None)
+    try:
+        from lora_normal_form_amd import workload as glue
+        ld = glue.load(wl, device=0)
+    finally:
+        if saved is not None:
+            os.environ["SCUTE_DECODE"] = saved
+    assert ld.batch.info()["path"] == 1
+    scute.scute_profile_enable(ld.layer.h, True)
+    ld.y.fill_(float("nan"))
+    ld.layer.forward(ld.batch, ld.x, ld.W, ld.y)
+    torch.cuda.synchronize()
+    names = set(scute.scute_profile_read(ld.layer.h))
+    scute.scute_profile_enable(ld.layer.h, False)
+    fused = kind == "ia3_vera_256"
+    assert ("fd_main" in names) == fused and ("decode_main" in names) == (not fused), names
+    _check(wl, ld.y.cpu().numpy().astype(np.float64))
+
+
 def test_decode_matches_generic_kernels():
     _need_gpu()
     wl = _wl(150, seed=12)
