@@ -3,7 +3,7 @@
 Builds an instrumented copy of the library in which thread 0 of every
 work-group of k_decode_main writes the 100 MHz real-time counter
 (s_memrealtime) at each phase boundary; nothing else changes, so the copy
-computes the same results. Then runs named workloads through it and prints,
+computes the same results. Then runs named workloads through it (on the two-launch decode path: SCUTE_DECODE=2) and prints,
 per phase, the median over work-groups of the time since the earliest
 work-group started (medians of five forwards):
 
@@ -103,6 +103,8 @@ def run(dest: str, workloads) -> None:
     if not os.path.exists(lib_path):
         raise SystemExit(f"{lib_path} missing: run `build` first")
     os.environ["SCUTE_LIB"] = lib_path
+    # the stamps are in the two-launch decode kernel: plan every batch there
+    os.environ["SCUTE_DECODE"] = "2"
     import numpy as np
     import torch
     sys.path.insert(0, ROOT)
