@@ -167,6 +167,39 @@ scute_status scute_load_adapter(scute_layer* layer, int32_t id,
                                 const scute_adapter_desc* desc,
                                 const void* W_host, void* stream);
 
+/* Split the layer's output columns into n_proj projections (at most 4) that
+ * share x and are computed by one GEMM over the stacked weight, e.g. q, k
+ * and v ("How does Scute plug into vLLM?", paper-daily.com explainer of
+ * "Scute: Exact Batched Serving for PEFT Adapters Beyond LoRA": OFT gives
+ * each projection its own input rotation, which is why Scute splits the
+ * q / k / v GEMM when OFT is present; with this call one GEMM keeps them).
+ * col_end[i] (HOST array) is the end column of projection i: increasing,
+ * every end but the last a multiple of 64, the last equal to d_out.
+ * Only while no adapter is loaded (SCUTE_E_STATE otherwise); plans built
+ * before become stale. n_proj = 1 with col_end[0] = d_out undoes it.
+ * Errors: SCUTE_E_SHAPE for bad ends or n_proj, SCUTE_E_INVALID for null. */
+scute_status scute_layer_set_projections(scute_layer* layer, int32_t n_proj,
+                                         const int64_t* col_end);
+
+/* Load adapter `id` like scute_load_adapter, with one rotation per
+ * projection of the layer: desc->method must be SCUTE_NORMAL_FORM with
+ * desc->R null, and R_proj[p] (HOST pointer, [d_in/blk][blk][blk] in
+ * desc->dtype, blk = desc->blk) is the rotation of projection p's input;
+ * a null R_proj[p] is the identity. Output columns of projection p compute
+ * ((x R_p) W) (.) s + b + the adapter's terms. Each P_p = R_p - I is stored
+ * like the single rotation slot, the n_proj of them one after another
+ * (scute_read_slot of SCUTE_SLOT_P returns n_proj d_in blk elements).
+ * Batches with such rows run the two-launch decode path (bf16, up to 256
+ * rows) or the generic kernels; scute_layer_forward_noalloc refuses them.
+ * Errors: SCUTE_E_STATE if the layer has one projection or `id` is
+ * occupied, SCUTE_E_INVALID for another method, a non-null desc->R or a
+ * null R_proj, SCUTE_E_SHAPE for a bad block size; otherwise as
+ * scute_load_adapter. */
+scute_status scute_load_adapter_proj(scute_layer* layer, int32_t id,
+                                     const scute_adapter_desc* desc,
+                                     const void* const* R_proj,
+                                     const void* W_host, void* stream);
+
 /* Unload adapter `id` and free its memory after `stream` drains.
  * SCUTE_E_STATE if `id` is not loaded. Plans built before become stale. */
 scute_status scute_unload_adapter(scute_layer* layer, int32_t id, void* stream);
@@ -264,7 +297,8 @@ scute_status scute_layer_forward(scute_layer* layer, const scute_batch* batch,
  * scratch than there is; SCUTE_E_INVALID for null or misaligned pointers
  * (16-byte x, W, y; 4-byte token_adapter); SCUTE_E_STATE if a VeRA adapter
  * is loaded and the shared pair is not set; SCUTE_E_UNSUPPORTED on a
- * host-only layer or a device index past 63. */
+ * host-only layer, a device index past 63, or a layer holding an adapter
+ * loaded with scute_load_adapter_proj. */
 scute_status scute_layer_forward_noalloc(scute_layer* layer, const int32_t* token_adapter,
                                          int32_t n, const void* x, const void* W, float* y,
                                          void* stream);

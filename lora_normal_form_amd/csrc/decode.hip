@@ -250,7 +250,8 @@ k_decode_prologue(ProArgs a) {
 // ---------------------------------------------------------------------------
 
 struct MainArgs {
-  const uint16_t* xs;               // [32 MGT][d_in] sorted x rows, then delta rows
+  const uint16_t* xs;               // [M_pad + 32 g_rot np][d_in] sorted x rows, then delta
+                                    // rows, one block of 32 g_rot rows per projection
   const uint16_t* W;
   const DecRow* rows;               // [M_pad]
   const DecStep* steps;             // expand steps by slice and row group
@@ -267,6 +268,7 @@ struct MainArgs {
   int32_t MG;
   int32_t g_rot, d_in, d_out, k_chunk, S, C, RT, AW;
   int32_t gv0, gv1, r_v;            // dense VeRA expand over row groups [gv0, gv1) (gv1 > gv0)
+  int32_t ptile[MAX_PROJ - 1];      // first column tile of projections 1.. (C past the last)
 };
 
 // Tile of the main kernel: 64 output columns (two 32-column MFMA blocks) by
@@ -680,14 +682,16 @@ k_decode_main(MainArgs a) {
   } else if constexpr (pre1) {
     load_w(wb[1], wrow, (int64_t)SK * min(1, nst - 1));
   }
-  // (2) row sources: staged row r (x rows, then delta rows) is row r of xs
+  // (2) row sources: staged row r (x rows, then delta rows) is row r of xs,
+  //     the delta rows taken from this tile's projection's block
   const uint16_t* src[2 * MGT];
   {
     const int piece = (lane & 7) ^ ((4 * cb + (lane >> 4)) & 7);
+    const int dsh = 32 * a.g_rot * ((c >= a.ptile[0]) + (c >= a.ptile[1]) + (c >= a.ptile[2]));
 #pragma unroll
     for (int q = 0; q < 2 * MGT; ++q) {
       const int r = 8 * (cb + 2 * q) + (lane >> 3);
-      src[q] = a.xs + (size_t)r * a.d_in + kbase + 8 * piece;
+      src[q] = a.xs + (size_t)(r + (r >= Mx ? dsh : 0)) * a.d_in + kbase + 8 * piece;
     }
   }
   stage_rows<MGT>(slot0 + kp * Cfg::STAGE, src, 0, cb);
@@ -1032,6 +1036,7 @@ scute_status launch_decode(scute_layer* L, const scute_batch* B, const void* x, 
   ma.gv0 = D.gv0;
   ma.gv1 = D.gv1;
   ma.r_v = L->r_v;
+  for (int32_t i = 0; i + 1 < MAX_PROJ; ++i) ma.ptile[i] = D.ptile[i];
   const dim3 grid(D.C, D.S);
   ProfScope ps(L, st, "decode_main", true);
   switch (D.MG + D.g_rot) {

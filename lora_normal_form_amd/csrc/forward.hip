@@ -54,32 +54,36 @@ __device__ __forceinline__ int32_t row_id(const int32_t* ra, int32_t p, const Sl
 }
 
 // ---------------------------------------------------------------------------
-// rotation: delta[p][col] = sum_i x[perm[p]][kb*blk + i] * P[kb][i][col - kb*blk],
-// P stored transposed per block; rows without a rotation get zero
-// grid (ceil(d_in / 256), rows)
+// rotation: delta[z][p][col] = sum_i x[perm[p]][kb*blk + i] * P_z[kb][i][col - kb*blk],
+// P stored transposed per block; rows without a rotation get zero. z is the
+// projection (grid z): an adapter that rotates per projection (F_RPROJ)
+// keeps P_z after P_0, one with a single rotation uses it for every z
+// grid (ceil(d_in / 256), rows, projections)
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k_rotate_ref(const T* __restrict__ x,
                                                     const int32_t* __restrict__ perm,
                                                     const int32_t* __restrict__ row_adapter,
                                                     const SlotEntry* __restrict__ table, int32_t na,
-                                                    int64_t d_in, T* __restrict__ delta) {
-  const int32_t p = blockIdx.y;
+                                                    int64_t d_in, int32_t n_rot, T* __restrict__ delta) {
+  const int32_t p = blockIdx.y, z = blockIdx.z;
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (col >= d_in) return;
+  const size_t o = ((size_t)z * n_rot + p) * d_in + col;
   const int32_t a = row_id(row_adapter, p, table, na);
   if (a < 0 || !(table[a].flags & F_R)) {
-    stf(delta, (size_t)p * d_in + col, 0.f);
+    stf(delta, o, 0.f);
     return;
   }
   const SlotEntry E = table[a];
   const int32_t blk = E.blk;
   const int64_t kb = col / blk, jj = col - kb * blk;
   const T* xr = x + (size_t)src_row(perm, p) * d_in + kb * blk;
-  const T* Pt = (const T*)E.P + ((size_t)kb * blk + jj) * blk;  // (R - I)^T row jj
+  const T* Pz = (const T*)E.P + ((E.flags & F_RPROJ) ? (size_t)z * d_in * blk : 0);
+  const T* Pt = Pz + ((size_t)kb * blk + jj) * blk;  // (R - I)^T row jj
   float acc = 0.f;
   for (int32_t i = 0; i < blk; ++i) acc += ldf(xr, i) * ldf(Pt, i);
-  stf(delta, (size_t)p * d_in + col, acc);
+  stf(delta, o, acc);
 }
 
 __device__ __forceinline__ float block_sum_256(float v, float* red) {
@@ -158,6 +162,17 @@ __global__ void __launch_bounds__(256) k_vera_shrink_ref(const T* __restrict__ x
 // grid (ceil(d_out/32), ceil(n/32)), 256 threads, 4 outputs per thread; a
 // row with an unusable adapter id gets NaN
 // ---------------------------------------------------------------------------
+// first column of projections 1, 2, 3 (d_out past the last)
+struct ProjStarts {
+  int64_t c[MAX_PROJ - 1];
+};
+
+static ProjStarts proj_starts(const scute_layer* L, bool rproj) {
+  ProjStarts ps;
+  for (int32_t i = 0; i + 1 < MAX_PROJ; ++i) ps.c[i] = rproj && i + 1 < L->n_proj ? L->proj_end[i] : L->d_out;
+  return ps;
+}
+
 template <typename T>
 __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const T* __restrict__ W,
                                                   const T* __restrict__ delta,
@@ -165,7 +180,7 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
                                                   const int32_t* __restrict__ row_adapter,
                                                   const SlotEntry* __restrict__ table, int32_t na,
                                                   int32_t n, int32_t n_rot, int64_t d_in, int64_t d_out,
-                                                  float* __restrict__ y) {
+                                                  ProjStarts ps, float* __restrict__ y) {
   // 128 k per round: every thread's 32 loads of a round are in flight
   // together, so a round costs one memory round trip
   constexpr int KR = 128;
@@ -178,6 +193,9 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
   const int64_t j0 = (int64_t)blockIdx.x * 32;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const int passes = (p0 < n_rot) ? 2 : 1;
+  // this block's projection picks the delta block (projection starts are
+  // multiples of 64, so the 32 columns lie in one projection)
+  const T* dz = delta + (size_t)((j0 >= ps.c[0]) + (j0 >= ps.c[1]) + (j0 >= ps.c[2])) * n_rot * d_in;
   for (int pass = 0; pass < passes; ++pass) {
     for (int64_t k0 = 0; k0 < d_in; k0 += KR) {
       for (int q = 0; q < 4; ++q) {
@@ -186,7 +204,7 @@ __global__ void __launch_bounds__(256) k_gemm_ref(const T* __restrict__ x, const
         const int64_t j = j0 + r;
         const bool xrow = pass == 0 ? p < n : p < n_rot;
         const T* xsrc = pass == 0 ? (p < n ? x + (size_t)src_row(perm, p) * d_in : x)
-                                  : delta + (size_t)min(p, max(n_rot - 1, 0)) * d_in;
+                                  : dz + (size_t)min(p, max(n_rot - 1, 0)) * d_in;
 #pragma unroll
         for (int cq = 0; cq < KR / 32; ++cq) {
           const int64_t kk = k0 + 32 * cq + tx;
@@ -279,8 +297,10 @@ static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x,
   int32_t nl = 0;
   if (B->n_rot > 0) {
     ProfScope ps(L, st, "rotate");
-    hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), B->n_rot), dim3(256), 0, st, x,
-                       B->d_perm, B->d_row_adapter, L->table_dev, L->max_adapters, d_in, (T*)B->delta);
+    const unsigned npz = B->rproj ? (unsigned)L->n_proj : 1u;
+    hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), B->n_rot, npz), dim3(256), 0, st, x,
+                       B->d_perm, B->d_row_adapter, L->table_dev, L->max_adapters, d_in, B->n_rot,
+                       (T*)B->delta);
     ++nl;
   }
   if (B->max_rank > 0) {
@@ -300,7 +320,7 @@ static scute_status launch_ref(scute_layer* L, const scute_batch* B, const T* x,
     ProfScope ps(L, st, "gemm");
     hipLaunchKernelGGL(k_gemm_ref<T>, dim3(cdiv(d_out, 32), cdiv(n, 32)), dim3(256), 0, st, x, W,
                        (const T*)B->delta, B->d_perm, B->d_row_adapter, L->table_dev, L->max_adapters,
-                       n, B->n_rot, d_in, d_out, y);
+                       n, B->n_rot, d_in, d_out, proj_starts(L, B->rproj), y);
     ++nl;
   }
   if (B->max_rank > 0 || B->n_vera > 0) {
@@ -493,14 +513,16 @@ void* g_scratch[NOALLOC_MAX_DEVICES] = {};
 void layer_facts(scute_layer* L) {
   if (L->na_epoch == L->epoch) return;
   int32_t rk = 0;
-  bool rot = false;
+  bool rot = false, rproj = false;
   for (const SlotEntry& E : L->table) {
     if (!(E.flags & F_LOADED)) continue;
     if ((E.flags & F_TERM) && E.rank > rk) rk = E.rank;
     if (E.flags & F_R) rot = true;
+    if (E.flags & F_RPROJ) rproj = true;
   }
   L->na_max_rank = rk;
   L->na_rot = rot;
+  L->na_rproj = rproj;
   L->na_epoch = L->epoch;
 }
 
@@ -515,7 +537,7 @@ void launch_noalloc(scute_layer* L, const int32_t* ta, int32_t n, const T* x, co
   float* u = (float*)(ws + o_u);
   if (L->na_rot)
     hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), n), dim3(256), 0, st, x, nullptr, ta,
-                       L->table_dev, na, d_in, delta);
+                       L->table_dev, na, d_in, n, delta);
   if (rk > 0)
     hipLaunchKernelGGL(k_shrink_ref<T>, dim3(rk, n), dim3(256), 0, st, x, nullptr, ta, L->table_dev, na,
                        d_in, rk, t);
@@ -523,7 +545,8 @@ void launch_noalloc(scute_layer* L, const int32_t* ta, int32_t n, const T* x, co
     hipLaunchKernelGGL(k_vera_shrink_ref<T>, dim3(L->r_v, n), dim3(256), 0, st, x, nullptr, ta, nullptr,
                        L->table_dev, na, (const T*)L->A_sh, d_in, L->r_v, u);
   hipLaunchKernelGGL(k_gemm_ref<T>, dim3(cdiv(d_out, 32), cdiv(n, 32)), dim3(256), 0, st, x, W,
-                     (const T*)delta, nullptr, ta, L->table_dev, na, n, L->na_rot ? n : 0, d_in, d_out, y);
+                     (const T*)delta, nullptr, ta, L->table_dev, na, n, L->na_rot ? n : 0, d_in, d_out,
+                     proj_starts(L, false), y);
   if (rk > 0 || vera)
     hipLaunchKernelGGL(k_expand_ref<T>, dim3(cdiv(d_out, 256), n), dim3(256), 0, st, t, u,
                        (const T*)L->B_sh, nullptr, ta, L->table_dev, na, rk, L->r_v, d_out, y);
@@ -564,6 +587,9 @@ extern "C" scute_status scute_layer_forward_noalloc(scute_layer* L, const int32_
     if (vera && (!L->A_sh || !L->B_sh))
       return fail(SCUTE_E_STATE, "scute_layer_forward_noalloc: shared VeRA pair not set");
     layer_facts(L);
+    if (L->na_rproj)
+      return fail(SCUTE_E_UNSUPPORTED,
+                  "scute_layer_forward_noalloc: an adapter rotates per projection (use scute_layer_forward)");
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     const size_t es = dtype_size(L->act);
     const size_t o_t = L->na_rot ? al((size_t)n * L->d_in * es) : 0;

@@ -20,7 +20,13 @@ enum : int32_t {
   F_B = 8,     // shift b
   F_TERM = 16, // own low-rank term (A', B')
   F_VERA = 32, // shared VeRA term (d, e live)
+  F_RPROJ = 64, // one rotation per projection: P holds n_proj stacked (R_p - I)
 };
+
+// Projections of a layer: output column ranges that share x and W's rows
+// but may each take their own input rotation (q, k and v over one stacked
+// weight). proj_end[i] is the end of projection i; at most 4.
+constexpr int32_t MAX_PROJ = 4;
 
 // Device-visible live-slot entry of one adapter (struct of pointers into
 // the adapter's library-owned storage). Unused pointers are null.
@@ -59,6 +65,8 @@ struct scute_layer {
   int64_t d_in = 0, d_out = 0;
   int32_t act = SCUTE_BF16;
   int32_t max_adapters = 0;
+  int32_t n_proj = 1;                   // output column ranges (scute_layer_set_projections)
+  int64_t proj_end[scute::MAX_PROJ] = {0, 0, 0, 0};
   std::vector<scute::SlotEntry> table;  // host mirror
   std::vector<scute::AdapterStore> store;
   scute::SlotEntry* table_dev = nullptr;
@@ -72,6 +80,7 @@ struct scute_layer {
   uint64_t na_epoch = 0;
   int32_t na_max_rank = 0;
   bool na_rot = false;
+  bool na_rproj = false;  // some loaded adapter rotates per projection
   // kernel timing (scute_profile_enable)
   bool profiling = false;
   std::vector<scute::ProfEvent> prof_pending;
@@ -167,7 +176,11 @@ struct DecodePlan {
   const DecVeraRow* vrows = nullptr;     // [32 nvb]
   const DecStep* steps = nullptr;        // [n_steps]
   const float* zeros = nullptr;          // [d_out] of 0.0f
-  uint16_t* xs = nullptr;     // [M_pad + 32 g_rot][d_in] bf16: sorted x rows, then delta rows
+  uint16_t* xs = nullptr;     // [M_pad + 32 g_rot np][d_in] bf16: sorted x rows, then delta rows
+                              // of each projection in turn
+  int32_t np = 1;             // delta row blocks (the layer's projections when a row's
+                              // adapter rotates per projection, else 1)
+  int32_t ptile[MAX_PROJ - 1] = {0, 0, 0};  // first column tile of projections 1.. (C past the last)
   float* acc32[2] = {nullptr, nullptr};  // per parity: [M_pad][AW] fp32 shrink sums
   float* part = nullptr;      // [S][C][M_pad][64] split-K partial tiles (S > 1)
   int32_t* cnt = nullptr;     // [C] arrival counters (kept at zero)
@@ -336,6 +349,7 @@ struct scute_batch {
   int32_t n_vera = 0;     // rows with a VeRA term
   int32_t max_rank = 0;   // largest own-term rank among touched adapters
   int32_t n_touched = 0;
+  bool rproj = false;     // some row's adapter rotates per projection (F_RPROJ)
   // host tables
   std::vector<int32_t> perm;         // [n] token at sorted position
   std::vector<int32_t> row_adapter;  // [n] adapter of sorted position (-1)
@@ -348,7 +362,8 @@ struct scute_batch {
   int32_t* d_seg = nullptr;
   int32_t* d_vera_pos = nullptr;
   void* ws = nullptr;         // workspace allocation
-  void* delta = nullptr;      // [n_rot][d_in] act dtype: x (R - I)
+  void* delta = nullptr;      // [np][n_rot][d_in] act dtype: x (R_p - I), np = the layer's
+                              // projections when rproj, else 1
   float* t = nullptr;         // [n][max_rank]  own-term shrink
   float* u = nullptr;         // [n][r_v] VeRA shrink scaled by d (rows with VeRA)
   void* fast_dev = nullptr;   // decode-path tables + workspaces (one allocation)

@@ -227,6 +227,7 @@ extern "C" scute_status scute_layer_create(int32_t device, int64_t d_in, int64_t
     L->device = device;
     L->d_in = d_in;
     L->d_out = d_out;
+    L->proj_end[0] = d_out;
     L->act = act_dtype;
     L->max_adapters = max_adapters;
     L->table.assign(max_adapters, SlotEntry{});
@@ -325,6 +326,41 @@ struct FoldOut {
   std::vector<uint8_t> A, B, P;      // act dtype bytes
   std::vector<float> s, b, vd, ve;   // float32
 };
+
+// One rotation slot, (R - I)^T per block in the activation dtype, into dst
+// (d_in blk elements): R given directly, or as the Cayley transform of the
+// skew blocks Q ("The big picture": OFT's rotation is a Cayley transform).
+scute_status fold_rotation(const scute_layer* L, int32_t dt, int32_t blk, const void* src, bool cayley,
+                           uint8_t* dst) {
+  const int64_t nb = L->d_in / blk;
+  std::vector<double> M((size_t)blk * blk), X((size_t)blk * blk);
+  for (int64_t kb = 0; kb < nb; ++kb) {
+    const size_t base = (size_t)kb * blk * blk;
+    if (cayley) {
+      // R = (I - Q)^-1 (I + Q)
+      for (int32_t i = 0; i < blk; ++i)
+        for (int32_t j = 0; j < blk; ++j) {
+          double q = load_elem(src, dt, base + (size_t)i * blk + j);
+          double id = (i == j) ? 1.0 : 0.0;
+          M[(size_t)i * blk + j] = id - q;
+          X[(size_t)i * blk + j] = id + q;
+        }
+      if (!solve_dense(blk, M, X))
+        return fail(SCUTE_E_INVALID, "scute_load_adapter: I - Q is singular");
+    } else if (src) {
+      for (int32_t i = 0; i < blk * blk; ++i) X[i] = load_elem(src, dt, base + i);
+    } else {  // identity
+      for (int32_t i = 0; i < blk; ++i)
+        for (int32_t j = 0; j < blk; ++j) X[(size_t)i * blk + j] = (i == j) ? 1.0 : 0.0;
+    }
+    // stored transposed, (R - I)^T: element [kb][j][i] = (R - I)[kb][i][j],
+    // so one output column's block entries are contiguous
+    for (int32_t i = 0; i < blk; ++i)
+      for (int32_t j = 0; j < blk; ++j)
+        store_act(dst, L->act, base + (size_t)j * blk + i, X[(size_t)i * blk + j] - ((i == j) ? 1.0 : 0.0));
+  }
+  return SCUTE_OK;
+}
 
 scute_status fold_adapter(const scute_layer* L, const scute_adapter_desc* D, const void* W_host,
                           FoldOut& F) {
@@ -430,34 +466,92 @@ scute_status fold_adapter(const scute_layer* L, const scute_adapter_desc* D, con
     scute_status st;
     if ((st = need(meth == SCUTE_OFT ? D->Q : D->R, meth == SCUTE_OFT ? "Q" : "R"))) return st;
     F.blk = blk;
-    const int64_t nb = d_in / blk;
     F.P.resize((size_t)d_in * blk * es);
-    std::vector<double> M((size_t)blk * blk), X((size_t)blk * blk);
-    for (int64_t kb = 0; kb < nb; ++kb) {
-      const size_t base = (size_t)kb * blk * blk;
-      if (meth == SCUTE_OFT) {
-        // Cayley transform of the skew block: R = (I - Q)^-1 (I + Q)
-        for (int32_t i = 0; i < blk; ++i)
-          for (int32_t j = 0; j < blk; ++j) {
-            double q = load_elem(D->Q, dt, base + (size_t)i * blk + j);
-            double id = (i == j) ? 1.0 : 0.0;
-            M[(size_t)i * blk + j] = id - q;
-            X[(size_t)i * blk + j] = id + q;
-          }
-        if (!solve_dense(blk, M, X))
-          return fail(SCUTE_E_INVALID, "scute_load_adapter: I - Q is singular");
-      } else {
-        for (int32_t i = 0; i < blk * blk; ++i) X[i] = load_elem(D->R, dt, base + i);
-      }
-      // stored transposed, (R - I)^T: element [kb][j][i] = (R - I)[kb][i][j],
-      // so one output column's block entries are contiguous
-      for (int32_t i = 0; i < blk; ++i)
-        for (int32_t j = 0; j < blk; ++j)
-          store_act(F.P.data(), act, base + (size_t)j * blk + i,
-                    X[(size_t)i * blk + j] - ((i == j) ? 1.0 : 0.0));
-    }
+    if ((st = fold_rotation(L, dt, blk, meth == SCUTE_OFT ? D->Q : D->R, meth == SCUTE_OFT, F.P.data())))
+      return st;
     F.flags |= F_R;
   }
+  return SCUTE_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Lay out every folded slot in one allocation (256-byte aligned parts),
+// upload it and publish the slot entry.
+scute_status store_adapter(scute_layer* L, int32_t id, const FoldOut& F, int32_t method, void* stream) {
+  // lay out every slot in one allocation, 256-byte aligned parts
+  AdapterStore S;
+  const size_t es = dtype_size(L->act);
+  size_t lens[7] = {F.A.size(), F.B.size(), F.s.size() * 4, F.b.size() * 4,
+                    F.vd.size() * 4, F.ve.size() * 4, F.P.size()};
+  size_t off = 0;
+  for (int i = 0; i < 7; ++i) {
+    S.off[i] = off;
+    S.len[i] = lens[i];
+    off += (lens[i] + 255) & ~(size_t)255;
+  }
+  S.bytes = std::max<size_t>(off, 256);
+  std::vector<uint8_t> host(S.bytes, 0);
+  const void* srcs[7] = {F.A.data(), F.B.data(), F.s.data(), F.b.data(),
+                         F.vd.data(), F.ve.data(), F.P.data()};
+  for (int i = 0; i < 7; ++i)
+    if (lens[i]) memcpy(host.data() + S.off[i], srcs[i], lens[i]);
+  (void)es;
+
+  if (L->device >= 0) {
+    DeviceGuard g(L->device);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMalloc(&S.mem, S.bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(adapter)");
+    e = hipMemcpyAsync(S.mem, host.data(), S.bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      (void)hipFree(S.mem);
+      return hip_fail(e, "upload adapter");
+    }
+  } else {
+    S.mem = malloc(S.bytes);
+    if (!S.mem) return fail(SCUTE_E_NOMEM, "scute_load_adapter: host allocation failed");
+    memcpy(S.mem, host.data(), S.bytes);
+  }
+
+  SlotEntry E{};
+  auto part = [&](int i) -> void* { return S.len[i] ? (uint8_t*)S.mem + S.off[i] : nullptr; };
+  E.A = part(SCUTE_SLOT_A);
+  E.B = part(SCUTE_SLOT_B);
+  E.s = (const float*)part(SCUTE_SLOT_S);
+  E.b = (const float*)part(SCUTE_SLOT_BIAS);
+  E.vd = (const float*)part(SCUTE_SLOT_VD);
+  E.ve = (const float*)part(SCUTE_SLOT_VE);
+  E.P = part(SCUTE_SLOT_P);
+  E.rank = F.rank;
+  E.blk = F.blk;
+  E.flags = F.flags | F_LOADED;
+  E.method = method;
+
+  if (L->device >= 0) {
+    DeviceGuard g(L->device);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(L->table_dev + id, &E, sizeof(E), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      (void)hipFree(S.mem);
+      return hip_fail(e, "upload slot entry");
+    }
+  }
+  L->table[id] = E;
+  L->store[id] = S;
+  if (E.flags & F_VERA) L->n_vera_loaded++;
+  L->epoch++;
+  return SCUTE_OK;
+}
+
+scute_status load_checks(const scute_layer* L, int32_t id, const void* D, const char* fn) {
+  if (!L || !D) return fail(SCUTE_E_INVALID, std::string(fn) + ": null argument");
+  if (id < 0 || id >= L->max_adapters) return fail(SCUTE_E_INVALID, std::string(fn) + ": id out of range");
+  if (L->table[id].flags & F_LOADED) return fail(SCUTE_E_STATE, std::string(fn) + ": id is occupied");
   return SCUTE_OK;
 }
 
@@ -466,85 +560,71 @@ scute_status fold_adapter(const scute_layer* L, const scute_adapter_desc* D, con
 extern "C" scute_status scute_load_adapter(scute_layer* L, int32_t id, const scute_adapter_desc* D,
                                            const void* W_host, void* stream) {
   try {
-    if (!L || !D) return fail(SCUTE_E_INVALID, "scute_load_adapter: null argument");
-    if (id < 0 || id >= L->max_adapters)
-      return fail(SCUTE_E_INVALID, "scute_load_adapter: id out of range");
-    if (L->table[id].flags & F_LOADED)
-      return fail(SCUTE_E_STATE, "scute_load_adapter: id is occupied");
-    FoldOut F;
-    scute_status st = fold_adapter(L, D, W_host, F);
+    scute_status st = load_checks(L, id, D, "scute_load_adapter");
     if (st != SCUTE_OK) return st;
-
-    // lay out every slot in one allocation, 256-byte aligned parts
-    AdapterStore S;
-    const size_t es = dtype_size(L->act);
-    size_t lens[7] = {F.A.size(), F.B.size(), F.s.size() * 4, F.b.size() * 4,
-                      F.vd.size() * 4, F.ve.size() * 4, F.P.size()};
-    size_t off = 0;
-    for (int i = 0; i < 7; ++i) {
-      S.off[i] = off;
-      S.len[i] = lens[i];
-      off += (lens[i] + 255) & ~(size_t)255;
-    }
-    S.bytes = std::max<size_t>(off, 256);
-    std::vector<uint8_t> host(S.bytes, 0);
-    const void* srcs[7] = {F.A.data(), F.B.data(), F.s.data(), F.b.data(),
-                           F.vd.data(), F.ve.data(), F.P.data()};
-    for (int i = 0; i < 7; ++i)
-      if (lens[i]) memcpy(host.data() + S.off[i], srcs[i], lens[i]);
-    (void)es;
-
-    if (L->device >= 0) {
-      DeviceGuard g(L->device);
-      hipStream_t s = (hipStream_t)stream;
-      hipError_t e = hipMalloc(&S.mem, S.bytes);
-      if (e != hipSuccess) return hip_fail(e, "hipMalloc(adapter)");
-      e = hipMemcpyAsync(S.mem, host.data(), S.bytes, hipMemcpyHostToDevice, s);
-      if (e == hipSuccess) e = hipStreamSynchronize(s);
-      if (e != hipSuccess) {
-        (void)hipFree(S.mem);
-        return hip_fail(e, "upload adapter");
-      }
-    } else {
-      S.mem = malloc(S.bytes);
-      if (!S.mem) return fail(SCUTE_E_NOMEM, "scute_load_adapter: host allocation failed");
-      memcpy(S.mem, host.data(), S.bytes);
-    }
-
-    SlotEntry E{};
-    auto part = [&](int i) -> void* { return S.len[i] ? (uint8_t*)S.mem + S.off[i] : nullptr; };
-    E.A = part(SCUTE_SLOT_A);
-    E.B = part(SCUTE_SLOT_B);
-    E.s = (const float*)part(SCUTE_SLOT_S);
-    E.b = (const float*)part(SCUTE_SLOT_BIAS);
-    E.vd = (const float*)part(SCUTE_SLOT_VD);
-    E.ve = (const float*)part(SCUTE_SLOT_VE);
-    E.P = part(SCUTE_SLOT_P);
-    E.rank = F.rank;
-    E.blk = F.blk;
-    E.flags = F.flags | F_LOADED;
-    E.method = D->method;
-
-    if (L->device >= 0) {
-      DeviceGuard g(L->device);
-      hipStream_t s = (hipStream_t)stream;
-      hipError_t e = hipMemcpyAsync(L->table_dev + id, &E, sizeof(E), hipMemcpyHostToDevice, s);
-      if (e == hipSuccess) e = hipStreamSynchronize(s);
-      if (e != hipSuccess) {
-        (void)hipFree(S.mem);
-        return hip_fail(e, "upload slot entry");
-      }
-    }
-    L->table[id] = E;
-    L->store[id] = S;
-    if (E.flags & F_VERA) L->n_vera_loaded++;
-    L->epoch++;
-    return SCUTE_OK;
+    FoldOut F;
+    st = fold_adapter(L, D, W_host, F);
+    if (st != SCUTE_OK) return st;
+    return store_adapter(L, id, F, D->method, stream);
   } catch (const std::bad_alloc&) {
     return fail(SCUTE_E_NOMEM, "scute_load_adapter: host allocation failed");
   } catch (...) {
     return fail(SCUTE_E_INVALID, "scute_load_adapter: unexpected error");
   }
+}
+
+extern "C" scute_status scute_load_adapter_proj(scute_layer* L, int32_t id, const scute_adapter_desc* D,
+                                                const void* const* R_proj, const void* W_host,
+                                                void* stream) {
+  try {
+    scute_status st = load_checks(L, id, D, "scute_load_adapter_proj");
+    if (st != SCUTE_OK) return st;
+    if (L->n_proj < 2)
+      return fail(SCUTE_E_STATE, "scute_load_adapter_proj: the layer has no projections");
+    if (D->method != SCUTE_NORMAL_FORM || D->R)
+      return fail(SCUTE_E_INVALID, "scute_load_adapter_proj: desc must be NORMAL_FORM with R null");
+    if (!R_proj) return fail(SCUTE_E_INVALID, "scute_load_adapter_proj: R_proj is null");
+    const int32_t blk = D->blk;
+    if (blk <= 0 || blk > 256 || L->d_in % blk != 0)
+      return fail(SCUTE_E_SHAPE, "scute_load_adapter_proj: blk must be in [1, 256] and divide d_in");
+    if (dtype_size(D->dtype) == 0) return fail(SCUTE_E_INVALID, "scute_load_adapter_proj: bad desc dtype");
+    FoldOut F;
+    st = fold_adapter(L, D, W_host, F);
+    if (st != SCUTE_OK) return st;
+    const size_t one = (size_t)L->d_in * blk * dtype_size(L->act);
+    F.blk = blk;
+    F.P.assign(one * L->n_proj, 0);
+    for (int32_t p = 0; p < L->n_proj; ++p)
+      if ((st = fold_rotation(L, D->dtype, blk, R_proj[p], false, F.P.data() + one * p))) return st;
+    F.flags |= F_R | F_RPROJ;
+    return store_adapter(L, id, F, D->method, stream);
+  } catch (const std::bad_alloc&) {
+    return fail(SCUTE_E_NOMEM, "scute_load_adapter_proj: host allocation failed");
+  } catch (...) {
+    return fail(SCUTE_E_INVALID, "scute_load_adapter_proj: unexpected error");
+  }
+}
+
+extern "C" scute_status scute_layer_set_projections(scute_layer* L, int32_t n_proj, const int64_t* col_end) {
+  if (!L || !col_end) return fail(SCUTE_E_INVALID, "scute_layer_set_projections: null argument");
+  if (n_proj < 1 || n_proj > MAX_PROJ)
+    return fail(SCUTE_E_SHAPE, "scute_layer_set_projections: n_proj must be in [1, 4]");
+  for (const SlotEntry& E : L->table)
+    if (E.flags & F_LOADED)
+      return fail(SCUTE_E_STATE, "scute_layer_set_projections: unload every adapter first");
+  int64_t prev = 0;
+  for (int32_t i = 0; i < n_proj; ++i) {
+    const int64_t e = col_end[i];
+    if (e <= prev || e > L->d_out || (i + 1 < n_proj && e % 64 != 0))
+      return fail(SCUTE_E_SHAPE,
+                  "scute_layer_set_projections: ends must increase, and all but the last be multiples of 64");
+    prev = e;
+  }
+  if (prev != L->d_out) return fail(SCUTE_E_SHAPE, "scute_layer_set_projections: the last end must be d_out");
+  L->n_proj = n_proj;
+  for (int32_t i = 0; i < MAX_PROJ; ++i) L->proj_end[i] = i < n_proj ? col_end[i] : L->d_out;
+  L->epoch++;
+  return SCUTE_OK;
 }
 
 extern "C" scute_status scute_unload_adapter(scute_layer* L, int32_t id, void* stream) {
@@ -606,7 +686,8 @@ extern "C" scute_status scute_read_slot(const scute_layer* L, int32_t id, int32_
   if (slot == SCUTE_SLOT_P) {
     // storage holds (R - I)^T per block; hand back R - I
     const int32_t blk = L->table[id].blk;
-    const size_t es = dtype_size(L->act), nb = (size_t)L->d_in / blk;
+    // (n_proj stacked rotations when the adapter rotates per projection)
+    const size_t es = dtype_size(L->act), nb = S.len[slot] / ((size_t)blk * blk * es);
     std::vector<uint8_t> blkbuf((size_t)blk * blk * es);
     for (size_t kb = 0; kb < nb; ++kb) {
       uint8_t* b = (uint8_t*)dst + kb * blk * blk * es;

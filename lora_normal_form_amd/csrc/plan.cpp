@@ -101,6 +101,7 @@ extern "C" scute_status scute_plan_batch_flags(scute_layer* L, const int32_t* to
       if (a < 0) continue;
       const SlotEntry& E = L->table[a];
       if (E.flags & F_R) B->n_rot = p + 1;
+      if (E.flags & F_RPROJ) B->rproj = true;
       if (E.flags & F_VERA) B->vera_pos.push_back(p);
       if ((E.flags & F_TERM) && E.rank > B->max_rank) B->max_rank = E.rank;
       if (!touched[a]) {
@@ -150,7 +151,8 @@ extern "C" scute_status scute_plan_batch_flags(scute_layer* L, const int32_t* to
       if (e == hipSuccess) e = hipStreamSynchronize(s);
       // workspaces
       size_t es = dtype_size(L->act);
-      size_t w_delta = al((size_t)B->n_rot * L->d_in * es);
+      // (one delta block per projection when a row rotates per projection)
+      size_t w_delta = al((size_t)(B->rproj ? L->n_proj : 1) * B->n_rot * L->d_in * es);
       size_t w_t = al((size_t)n * B->max_rank * 4);
       size_t w_u = B->n_vera ? al((size_t)n * L->r_v * 4) : 0;
       size_t wtot = w_delta + w_t + w_u;
@@ -255,7 +257,8 @@ extern "C" scute_status scute_cost_model(const scute_layer* L, const scute_batch
       flops_extra += 2.0 * (din * L->r_v + L->r_v * dout);
       exp_flops += 2.0 * L->r_v * dout;
     }
-    if (E.flags & F_R) flops_extra += 2.0 * din * E.blk;
+    // (x R_p for every projection p when the adapter rotates per projection)
+    if (E.flags & F_R) flops_extra += 2.0 * din * E.blk * ((E.flags & F_RPROJ) ? L->n_proj : 1);
   }
   if (any_vera) adapter += (double)L->r_v * (din + dout) * es;
   const double xwy = n * din * es + din * dout * es + n * dout * 4.0;

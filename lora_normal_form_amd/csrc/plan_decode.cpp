@@ -52,6 +52,8 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const bool own_fused = !(route & SCUTE_PLAN_ROUTE_EXPAND_PASS);
   const bool vera_fused = !(route & (SCUTE_PLAN_ROUTE_EXPAND_PASS | SCUTE_PLAN_ROUTE_VERA_PASS));
   if (L->act != SCUTE_BF16 || n <= 0 || n > 256) return SCUTE_OK;
+  // the route variants' rotation pass has one delta block
+  if (B->rproj && route) return SCUTE_OK;
   // K parts of the shrinks: at most 8 of 1024 (own) and 16 of 512 (VeRA)
   if (d_in % 128 != 0 || d_in > 8192 || d_out % 64 != 0) return SCUTE_OK;
   // W is addressed through a buffer range with 32-bit offsets
@@ -72,6 +74,12 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
     return SCUTE_OK;
   }
   D.M_pad = 32 * D.MG;
+  // rows that rotate per projection: one block of delta rows per projection,
+  // and each column tile stages its projection's block (projection ends are
+  // multiples of 64, so a tile lies in one projection)
+  D.np = B->rproj ? L->n_proj : 1;
+  for (int32_t i = 0; i + 1 < MAX_PROJ; ++i)
+    D.ptile[i] = i + 1 < D.np ? (int32_t)(L->proj_end[i] / 64) : (int32_t)(d_out / 64);
   D.RT = (B->max_rank + 15) / 16 * 16;
   D.C = (int32_t)(d_out / 64);
   // K slices: none when the column tiles alone nearly fill the chip (every
@@ -93,7 +101,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
-    if ((E.flags & F_R) && rot_in_pro) n_rot_items += (len + 3) / 4 * (int32_t)(d_in / 64);
+    if ((E.flags & F_R) && rot_in_pro) n_rot_items += D.np * ((len + 3) / 4) * (int32_t)(d_in / 64);
     if (E.flags & F_TERM) n_sgroups += (len + 3) / 4 * ((E.rank + 3) / 4);
   }
   const int32_t KQ = (int32_t)((d_in + 1023) / 1024);
@@ -255,7 +263,7 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   const size_t o_zeros = take(4 * (size_t)d_out);
   const size_t acc_bytes = 4 * (size_t)D.M_pad * D.AW;
   const size_t part_bytes = S > 1 ? 4 * (size_t)S * D.C * D.M_pad * 64 : 0;
-  const size_t xs_bytes = 2 * (size_t)(D.M_pad + 32 * D.g_rot) * d_in;
+  const size_t xs_bytes = 2 * (size_t)(D.M_pad + 32 * D.g_rot * D.np) * d_in;
   if (part_bytes >= ((size_t)1 << 31) || acc_bytes >= ((size_t)1 << 31)) {
     D = DecodePlan{};  // buffer offsets are 32-bit
     return SCUTE_OK;
@@ -307,19 +315,23 @@ scute_status build_decode_plan(const scute_layer* L, scute_batch* B, hipStream_t
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
+    // (projection pj's delta rows start 32 g_rot pj rows after the first
+    // block; an adapter with one rotation uses it for every projection)
     if ((E.flags & F_R) && rot_in_pro)
-      for (int32_t r0 = 0; r0 < len; r0 += 4)
-        for (int64_t c0 = 0; c0 < d_in; c0 += 64) {
-          DecProItem it{};
-          it.type = PRO_ROT;
-          it.p0 = start + r0;
-          it.n = std::min(4, len - r0);
-          it.k = (int32_t)c0;
-          toks(it);
-          it.ptr = (const uint16_t*)E.P;
-          it.blk = E.blk;
-          pro.push_back(it);
-        }
+      for (int32_t pj = 0; pj < D.np; ++pj)
+        for (int32_t r0 = 0; r0 < len; r0 += 4)
+          for (int64_t c0 = 0; c0 < d_in; c0 += 64) {
+            DecProItem it{};
+            it.type = PRO_ROT;
+            it.p0 = start + r0;
+            it.n = std::min(4, len - r0);
+            it.k = (int32_t)c0;
+            toks(it);
+            it.p0 += 32 * D.g_rot * pj;
+            it.ptr = (const uint16_t*)E.P + ((E.flags & F_RPROJ) ? (size_t)pj * d_in * E.blk : 0);
+            it.blk = E.blk;
+            pro.push_back(it);
+          }
     if (E.flags & F_TERM)
       for (int32_t r0 = 0; r0 < len; r0 += 4)
         for (int32_t k = 0; k < E.rank; k += 4) {

@@ -47,6 +47,9 @@ scute_status build_fdecode_plan(const scute_layer* L, scute_batch* B, hipStream_
   const bool det = (B->flags & SCUTE_PLAN_DETERMINISTIC) != 0;
   if (mode == 0 || (mode != 1 && mode != -1 && !det)) return SCUTE_OK;
   if (L->act != SCUTE_BF16 || n <= 0 || n > 256) return SCUTE_OK;
+  // rows that rotate per projection take the two-launch decode path or the
+  // generic kernels
+  if (B->rproj) return SCUTE_OK;
   if (d_in % 64 != 0 || d_out % 32 != 0) return SCUTE_OK;
   // W, x and every workspace are addressed through buffer ranges with
   // 32-bit offsets

@@ -39,6 +39,9 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   const int64_t d_in = L->d_in, d_out = L->d_out;
   if (env_int("SCUTE_PREFILL", 1) == 0) return SCUTE_OK;
   if (L->act != SCUTE_BF16 || n <= 0) return SCUTE_OK;
+  // rows that rotate per projection take the two-launch decode path or the
+  // generic kernels
+  if (B->rproj) return SCUTE_OK;
   // the main kernel's K loop runs in stages of 64 k (unrolled at compile
   // time for d_in 4096); the prologue's items need d_in % 256 (checked below)
   if (d_in % 64 != 0 || d_out % 256 != 0) return SCUTE_OK;

@@ -14,10 +14,14 @@ QKV, fused   one layer over W_qkv = [W_q; W_k; W_v] ([d_q + d_k + d_v][d_in]).
              Each tenant's per-projection slots, as the library folds them
              (read back with scute_read_slot), become one normal-form
              adapter: s and b concatenated (ones / zeros on projections the
-             tenant leaves alone) and one own term with the A' stacked and
-             the B' block diagonal (its rank the sum of theirs). Exact; not
-             possible when a tenant rotates or has a VeRA term (a different
-             input transform or shared pair per projection).
+             tenant leaves alone), one own term with the A' stacked and the
+             B' block diagonal (its rank the sum of theirs), and, when the
+             tenant rotates, one rotation per projection (the identity where
+             it does not): the layer's projections are set to the q / k / v
+             column ranges and the adapter loads with
+             scute_load_adapter_proj, so OFT tenants keep the single GEMM.
+             Exact; not possible with a VeRA term (a different shared pair
+             per projection).
 QKV, split   three layers and three forwards; any method.
 FFN          a gate layer (base weight only) and the up layer with the
              tenants' adapters ((IA)^3's l on its s slot), then
@@ -92,15 +96,20 @@ class QKVSplit:
 
 def fused_slots(per_proj, d_outs):
     """One normal-form adapter's arrays from a tenant's per-projection folded
-    slots (None for a projection it leaves alone)."""
+    slots (None for a projection it leaves alone). "R_proj" is None when no
+    projection rotates, else one rotation per projection (None: identity)."""
     d_in = None
     for sl in per_proj:
         if sl is None:
             continue
-        if sl["R_minus_I"] is not None or sl["vd"] is not None:
-            raise ValueError("a rotation or a VeRA term needs the split q / k / v layers")
+        if sl["vd"] is not None:
+            raise ValueError("a VeRA term needs the split q / k / v layers")
         if sl["A"] is not None:
             d_in = sl["A"].shape[1]
+    rot = [sl is not None and sl["R_minus_I"] is not None for sl in per_proj]
+    blks = {sl["R_minus_I"].shape[1] for sl, r in zip(per_proj, rot) if r}
+    if len(blks) > 1:
+        raise ValueError("rotations of different block sizes need the split q / k / v layers")
     s = np.concatenate([sl["s"] if sl is not None and sl["s"] is not None else np.ones(d)
                         for sl, d in zip(per_proj, d_outs)])
     b = np.concatenate([sl["b"] if sl is not None and sl["b"] is not None else np.zeros(d)
@@ -108,7 +117,12 @@ def fused_slots(per_proj, d_outs):
     has_s = any(sl is not None and sl["s"] is not None for sl in per_proj)
     has_b = any(sl is not None and sl["b"] is not None for sl in per_proj)
     terms = [(p, sl["A"], sl["B"]) for p, sl in enumerate(per_proj) if sl is not None and sl["A"] is not None]
-    out = {"s": s if has_s else None, "b": b if has_b else None, "rank": 0, "A": None, "B": None}
+    out = {"s": s if has_s else None, "b": b if has_b else None, "rank": 0, "A": None, "B": None,
+           "R_proj": None, "blk": 0}
+    if blks:
+        blk = blks.pop()
+        out["blk"] = blk
+        out["R_proj"] = [np.eye(blk)[None] + sl["R_minus_I"] if r else None for sl, r in zip(per_proj, rot)]
     if terms:
         r = sum(A.shape[0] for _, A, _ in terms)
         A = np.zeros((r, d_in))
@@ -131,13 +145,21 @@ def fused_layer(wls, n_tenants, device=0):
     wl0 = wls[0][0]
     hosts = [glue.load(wl, device=-1, plan=False) for wl, _ in wls]
     layer = scute.Layer(wl0.d_in, sum(d_outs), wl0.dtype, max_adapters=max(1, n_tenants), device=device)
+    fused = []
     for t in range(n_tenants):
         per = [convert.slots(h.layer, ids[t], wl.d_in, wl.d_out, wl.vera_rank) if t in ids else None
                for (wl, ids), h in zip(wls, hosts)]
-        if all(p is None for p in per):
+        fused.append(None if all(p is None for p in per) else fused_slots(per, d_outs))
+    if any(f is not None and f["R_proj"] is not None for f in fused):
+        layer.set_projections(np.cumsum(d_outs))
+    for t, f in enumerate(fused):
+        if f is None:
             continue
-        f = fused_slots(per, d_outs)
-        layer.load(t, "nf", rank=f["rank"], c=1.0, A=f["A"], B=f["B"], s=f["s"], b=f["b"])
+        if f["R_proj"] is not None:
+            layer.load_proj(t, f["R_proj"], f["blk"], rank=f["rank"], c=1.0, A=f["A"], B=f["B"], s=f["s"],
+                            b=f["b"])
+        else:
+            layer.load(t, "nf", rank=f["rank"], c=1.0, A=f["A"], B=f["B"], s=f["s"], b=f["b"])
     for h in hosts:
         h.layer.close()
     return layer
@@ -145,7 +167,8 @@ def fused_layer(wls, n_tenants, device=0):
 
 class QKVFused:
     """q, k and v as one layer over the stacked weights (tenants without a
-    rotation or VeRA term); forward returns the three column slices."""
+    VeRA term; rotations per projection); forward returns the three column
+    slices."""
 
     def __init__(self, wls, tenant_of_token, n_tenants, device=0, flags=0):
         import torch
@@ -236,13 +259,12 @@ def run():
         sp = QKVSplit(wls)
         t_split = _time(torch, sp.forward)
         sp.close()
-        rows.append({"layer": "qkv", "tenants": "lora+dora+ia3(k,v)" + ("+oft" if with_oft else ""),
-                     "route": "split", "us": t_split})
-        if not with_oft:
-            fu = QKVFused(wls, tt, len(ten))
-            t_fused = _time(torch, fu.forward)
-            fu.close()
-            rows.append({"layer": "qkv", "tenants": "lora+dora+ia3(k,v)", "route": "fused", "us": t_fused})
+        name = "lora+dora+ia3(k,v)" + ("+oft" if with_oft else "")
+        rows.append({"layer": "qkv", "tenants": name, "route": "split", "us": t_split})
+        fu = QKVFused(wls, tt, len(ten))
+        t_fused = _time(torch, fu.forward)
+        fu.close()
+        rows.append({"layer": "qkv", "tenants": name, "route": "fused", "us": t_fused})
         print(f"multiproj: {rows[-1]}", file=sys.stderr, flush=True)
     from synth import make_config
     up = make_config(3)  # FFN up 4096 -> 14336, 256 tokens, (IA)^3 + VeRA tenants

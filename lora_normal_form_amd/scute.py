@@ -78,6 +78,8 @@ SIGNATURES = {
     "scute_layer_destroy": (C.c_int32, [_P]),
     "scute_set_vera_shared": (C.c_int32, [_P, _P, _P, C.c_int32]),
     "scute_load_adapter": (C.c_int32, [_P, C.c_int32, C.POINTER(AdapterDesc), _P, _P]),
+    "scute_load_adapter_proj": (C.c_int32, [_P, C.c_int32, C.POINTER(AdapterDesc), C.POINTER(_P), _P, _P]),
+    "scute_layer_set_projections": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_int64)]),
     "scute_unload_adapter": (C.c_int32, [_P, C.c_int32, _P]),
     "scute_plan_batch": (C.c_int32, [_P, _P, C.c_int32, _P, C.POINTER(_P)]),
     "scute_plan_batch_flags": (C.c_int32, [_P, _P, C.c_int32, C.c_uint32, _P, C.POINTER(_P)]),
@@ -173,6 +175,19 @@ def scute_set_vera_shared(layer: int, A_sh, B_sh, r_v: int) -> None:
 
 def scute_load_adapter(layer: int, id: int, desc: AdapterDesc, W_host=None, stream=None) -> None:
     _check(lib.scute_load_adapter(layer, id, C.byref(desc), _ptr(W_host), _stream_ptr(stream)))
+
+
+def scute_load_adapter_proj(layer: int, id: int, desc: AdapterDesc, R_proj, W_host=None,
+                            stream=None) -> None:
+    """R_proj: one host array per projection ([d_in/blk][blk][blk] in the
+    descriptor's dtype) or None for the identity."""
+    ptrs = (_P * len(R_proj))(*[_ptr(r) for r in R_proj])
+    _check(lib.scute_load_adapter_proj(layer, id, C.byref(desc), ptrs, _ptr(W_host), _stream_ptr(stream)))
+
+
+def scute_layer_set_projections(layer: int, col_end) -> None:
+    ends = (C.c_int64 * len(col_end))(*[int(e) for e in col_end])
+    _check(lib.scute_layer_set_projections(layer, len(col_end), ends))
 
 
 def scute_unload_adapter(layer: int, id: int, stream=None) -> None:
@@ -345,6 +360,18 @@ class Layer:
         w = None if W_host is None else np.ascontiguousarray(np.asarray(W_host, np.float64))
         scute_load_adapter(self.h, id, desc, w, stream)
         del keep
+
+    def load_proj(self, id, R_proj, blk, rank=0, c=1.0, W_host=None, stream=None, **arrays):
+        """A normal-form adapter with one rotation per projection (R_proj[p]:
+        [d_in/blk][blk][blk], None for the identity)."""
+        desc, keep = make_desc("nf", rank, blk, c, **arrays)
+        rs = [None if r is None else np.ascontiguousarray(np.asarray(r, dtype=np.float64)) for r in R_proj]
+        w = None if W_host is None else np.ascontiguousarray(np.asarray(W_host, np.float64))
+        scute_load_adapter_proj(self.h, id, desc, rs, w, stream)
+        del keep, rs
+
+    def set_projections(self, col_end):
+        scute_layer_set_projections(self.h, col_end)
 
     def unload(self, id, stream=None):
         scute_unload_adapter(self.h, id, stream)

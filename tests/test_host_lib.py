@@ -330,3 +330,60 @@ def test_sanitizer_build_instruments_host_code_only():
             if f.startswith("-fsanitize") or f.startswith("-fno-sanitize"):
                 assert i > 0 and flags[i - 1] == "-Xarch_host", flags
     assert B.LIB_SAN != B.LIB and B.BUILD_SAN != B.BUILD
+
+
+# --------------------------------------------------------------------------
+# projections: one rotation per output column range
+# --------------------------------------------------------------------------
+
+def _rot_blocks(rng, nb, blk):
+    out = []
+    for _ in range(nb):
+        q = rng.normal(0.0, 0.3, size=(blk, blk))
+        out.append(oracle.cayley(q - q.T))
+    return np.stack(out)
+
+
+def test_projections_state_and_per_projection_fold():
+    rng = np.random.default_rng(21)
+    L = scute.Layer(32, 192, "f32", max_adapters=4, device=-1)
+    R0, R2 = _rot_blocks(rng, 4, 8), _rot_blocks(rng, 4, 8)
+    s = rng.normal(1.0, 0.1, size=192)
+    # no projections yet
+    assert _err(L.load_proj, 0, [R0, None, R2], 8, s=s) == scute.E_STATE
+    # ends: increasing, all but the last multiples of 64, the last d_out, at most 4
+    assert _err(L.set_projections, [100, 192]) == scute.E_SHAPE
+    assert _err(L.set_projections, [128, 64, 192]) == scute.E_SHAPE
+    assert _err(L.set_projections, [64, 128]) == scute.E_SHAPE
+    assert _err(L.set_projections, [64, 128, 192, 192]) == scute.E_SHAPE
+    assert _err(L.set_projections, [64] * 5) == scute.E_SHAPE
+    L.set_projections([64, 128, 192])
+    # only normal-form descriptors without their own R, whole blocks
+    desc, keep = scute.make_desc("lora", 2, 8, 1.0, A=np.ones((2, 32)), B=np.ones((192, 2)))
+    assert _err(scute.scute_load_adapter_proj, L.h, 0, desc, [R0, None, R2]) == scute.E_INVALID
+    desc, keep = scute.make_desc("nf", 0, 8, 1.0, R=R0)
+    assert _err(scute.scute_load_adapter_proj, L.h, 0, desc, [R0, None, R2]) == scute.E_INVALID
+    assert _err(L.load_proj, 0, [R0, None, R2], 5) == scute.E_SHAPE
+    del keep
+    L.load_proj(0, [R0, None, R2], 8, s=s)
+    L.load(1, "lora", rank=2, A=np.ones((2, 32)), B=np.ones((192, 2)))
+    info = L.info(0)
+    assert info["has_R"] == 1 and info["has_s"] == 1 and info["blk"] == 8
+    P = L.read_slot(0, scute.SLOT_P, (3, 4, 8, 8), np.float32)
+    for pj, R in enumerate([R0, None, R2]):
+        want = np.zeros((4, 8, 8)) if R is None else R - np.eye(8)[None]
+        _check_stored(P[pj].astype(np.float64), want, "f32")
+    # projections change only while no adapter is loaded
+    assert _err(L.set_projections, [128, 192]) == scute.E_STATE
+    # cost: x R_p for each of the three projections
+    b = L.plan([0, 1, 0, -1])
+    c = L.cost(b)
+    assert c["n_rot_rows"] == 2
+    base = 2.0 * 4 * 32 * 192
+    r = L.info(1)["rank"]  # (stored rank, padded at load)
+    lora = 2.0 * (32 * r + r * 192)
+    assert np.isclose(c["flops"], base + lora + 2 * 3 * 2.0 * 32 * 8)
+    L.unload(0)
+    L.unload(1)
+    L.set_projections([192])  # one projection again
+    assert _err(L.load_proj, 0, [R0], 8) == scute.E_STATE

@@ -7,7 +7,7 @@ import pytest
 
 from synth import AdapterSpec
 
-from lora_normal_form_amd import convert, multiproj
+from lora_normal_form_amd import convert, multiproj, scute
 from lora_normal_form_amd import workload as glue
 
 L, Dr, I3 = AdapterSpec("lora", rank=4, bias=True), AdapterSpec("dora", rank=3), AdapterSpec("ia3")
@@ -42,8 +42,35 @@ def test_fused_qkv_adapter_is_the_projections_side_by_side(dtype):
     fused.close()
 
 
-def test_fused_qkv_refuses_rotation():
+def test_fused_qkv_keeps_a_rotation_per_projection():
+    """OFT tenants: the fused adapter holds each projection's own rotation
+    (the identity where the tenant does not rotate), and its other slots are
+    the projections' side by side; a VeRA term still needs the split."""
     O = AdapterSpec("oft", blk=8)
-    wls, _ = multiproj.projection_workloads([(O, O, O)], 4, 32, (8, 8, 8), seed=4, dtype="f32")
+    ten = [(O, O, O), (O, None, L), (L, O, I3)]
+    d_outs = (64, 64, 128)
+    wls, _ = multiproj.projection_workloads(ten, 6, 32, d_outs, seed=4, dtype="f32")
+    fused = multiproj.fused_layer(wls, len(ten), device=-1)
+    offs = np.concatenate([[0], np.cumsum(d_outs)])
+    for t, per in enumerate(ten):
+        P = fused.read_slot(t, scute.SLOT_P, (3, 4, 8, 8), np.float32).astype(np.float64)
+        for p, (wl, ids) in enumerate(wls):
+            if per[p] is not None and per[p].method == "oft":
+                h = glue.load(wl, device=-1, plan=False)
+                want = convert.slots(h.layer, ids[t], wl.d_in, wl.d_out)["R_minus_I"]
+                h.layer.close()
+            else:
+                want = np.zeros((4, 8, 8))
+            assert np.allclose(P[p], want, rtol=0, atol=1e-6), (t, p)
+        # b and s side by side, as without rotations
+        info = fused.info(t)
+        if info["has_s"]:
+            s_f = fused.read_slot(t, scute.SLOT_S, (sum(d_outs),), np.float32)
+            for p, (wl, ids) in enumerate(wls):
+                if per[p] is not None and per[p].method == "ia3":
+                    assert np.allclose(s_f[offs[p]:offs[p + 1]], wl.adapters[ids[t]].l, atol=1e-6)
+    fused.close()
+    V = AdapterSpec("vera")
+    wls, _ = multiproj.projection_workloads([(O, V, O)], 4, 32, d_outs, seed=5, dtype="f32", vera_rank=4)
     with pytest.raises(ValueError):
         multiproj.fused_layer(wls, 1, device=-1)

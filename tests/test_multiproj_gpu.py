@@ -105,3 +105,39 @@ def test_gated_up_projection_with_ia3():
         want = (gg.double() * torch.sigmoid(gg.double()) * uu.double()).cpu().numpy()
         assert np.allclose(hh.cpu().numpy(), want, rtol=1e-5, atol=1e-6)
     gu.close()
+
+
+def test_qkv_fused_keeps_rotations_per_projection():
+    """OFT tenants in the fused q / k / v layer: one rotation per projection.
+    100 rows run the two-launch decode path (each column tile stages its
+    projection's delta rows), 300 rows the generic kernels (one delta block
+    per projection); both against the per-projection oracles and the split
+    layers. The no-allocation forward refuses such a layer."""
+    _need_gpu()
+    from lora_normal_form_amd import multiproj, scute
+    ten = [(L, L, L), (O, O, O), (None, I3, I3), (O, None, L), (Dr, O, None)] * 2
+    for n, path in ((100, 1), (300, 0)):
+        wls, tt = multiproj.projection_workloads(ten, n, 512, (512, 128, 256), seed=95 + n, none_frac=0.1)
+        print(f"\n[gpu] qkv fused with OFT tenants, {n} rows", flush=True)
+        fu = multiproj.QKVFused(wls, tt, len(ten))
+        assert fu.batch.info()["path"] == path
+        scute.scute_profile_enable(fu.layer.h, True)
+        yf = fu.forward()
+        torch.cuda.synchronize()
+        names = set(scute.scute_profile_read(fu.layer.h))
+        scute.scute_profile_enable(fu.layer.h, False)
+        assert ("decode_main" in names) == (path == 1) and "fd_main" not in names, names
+        sp = multiproj.QKVSplit(wls)
+        ys = sp.forward()
+        torch.cuda.synchronize()
+        for (wl, _), a, b in zip(wls, yf, ys):
+            fa = _check(wl, a)
+            fb = _check(wl, b)
+            assert np.max(np.abs(fa - fb)) <= 1e-2 * np.max(np.abs(fb))
+        if n == 100:
+            ta = torch.as_tensor(np.asarray(tt, dtype=np.int32), device="cuda:0")
+            with pytest.raises(scute.ScuteError) as e:
+                fu.layer.forward_noalloc(ta, fu.x, fu.W, fu.y)
+            assert e.value.code == scute.E_UNSUPPORTED
+        sp.close()
+        fu.close()
