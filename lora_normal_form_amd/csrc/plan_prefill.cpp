@@ -39,9 +39,11 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   const int64_t d_in = L->d_in, d_out = L->d_out;
   if (env_int("SCUTE_PREFILL", 1) == 0) return SCUTE_OK;
   if (L->act != SCUTE_BF16 || n <= 0) return SCUTE_OK;
-  // rows that rotate per projection take the two-launch decode path or the
-  // generic kernels
-  if (B->rproj) return SCUTE_OK;
+  // rows that rotate per projection: each 256-column tile stages its own
+  // projection's Delta rows, so the projections must end on tile boundaries
+  if (B->rproj)
+    for (int32_t i = 0; i + 1 < L->n_proj; ++i)
+      if (L->proj_end[i] % 256 != 0) return SCUTE_OK;
   // the main kernel's K loop runs in stages of 64 k (unrolled at compile
   // time for d_in 4096); the prologue's items need d_in % 256 (checked below)
   if (d_in % 64 != 0 || d_out % 256 != 0) return SCUTE_OK;
@@ -211,11 +213,16 @@ scute_status build_prefill_plan(const scute_layer* L, scute_batch* B, hipStream_
   for (int32_t i = 0; i < B->nseg(); ++i) {
     const int32_t a = B->seg[3 * i], start = B->seg[3 * i + 1], len = B->seg[3 * i + 2];
     const SlotEntry& E = L->table[a];
+    // (one Delta block of n_rot rows per projection when a row rotates per
+    // projection: pad is the block's first row; an adapter with one rotation
+    // uses it for every projection)
     if (E.flags & F_R)
-      for (int32_t r0 = 0; r0 < len; r0 += 32)
-        for (int64_t c0 = 0; c0 < d_in; c0 += 256)
-          pro.push_back(PfProItem{PP_ROT, start + r0, std::min(32, len - r0), (int32_t)c0,
-                                  (const uint16_t*)E.P, E.blk, 0});
+      for (int32_t pj = 0; pj < (B->rproj ? L->n_proj : 1); ++pj)
+        for (int32_t r0 = 0; r0 < len; r0 += 32)
+          for (int64_t c0 = 0; c0 < d_in; c0 += 256)
+            pro.push_back(PfProItem{PP_ROT, start + r0, std::min(32, len - r0), (int32_t)c0,
+                                    (const uint16_t*)E.P + ((E.flags & F_RPROJ) ? (size_t)pj * d_in * E.blk : 0),
+                                    E.blk, pj * B->n_rot});
   }
   P.n_pro = (int32_t)pro.size();
   // the prologue's items work in slices (shrinks) and column runs

@@ -53,7 +53,8 @@ namespace {
 
 struct PfArgs {
   const uint16_t* x;       // [n][d_in] rows in batch (token) order
-  const uint16_t* dx;      // [n_rot][d_in] Delta rows by sorted position
+  const uint16_t* dx;      // [np][n_rot][d_in] Delta rows by sorted position, one block per
+                           // projection (np = 1 unless a row rotates per projection)
   const uint16_t* W;       // [d_out][d_in]
   const PfChunk* chunks;   // [n_chunks]
   const int32_t* crow;     // [n_chunks][128] row sources: token, or -(Delta row) - 1
@@ -63,9 +64,11 @@ struct PfArgs {
   const int4* items;        // per work-group: column tile, chunk, K part (-1: all), exchange slot
   float* part;              // [n_split][P][32][256] f32x4 partial tiles
   int32_t* cnt;             // [n_split] arrival counters, kept at zero between forwards
-  uint32_t acc_bytes, x_bytes, dx_bytes, part_bytes;
+  uint32_t acc_bytes, x_bytes, dx_bytes, part_bytes;  // dx_bytes: one block
   int32_t d_in, d_out, RT, AW, r_v, P;
   int32_t nst;  // 64-k stages of the whole K dimension (d_in / 64)
+  int32_t n_rot;                // rows of a Delta block
+  int32_t ptile[MAX_PROJ - 1];  // first column tile of projections 1.. (past the last tile if none)
 };
 
 constexpr int PK = 64;              // k per stage
@@ -319,7 +322,10 @@ k_prefill_main(PfArgs a) {
     for (int v = 0; v < 4; ++v) {
       const int piece = (lane & 7) ^ ((4 * v + (lane >> 4)) & 7);
       srcv[v].rlo = make_rsrc(a.x, a.x_bytes);
-      srcv[v].rhi = rot ? make_rsrc(a.dx, a.dx_bytes) : srcv[v].rlo;
+      srcv[v].rhi = rot ? make_rsrc(a.dx + (size_t)((c >= a.ptile[0]) + (c >= a.ptile[1]) + (c >= a.ptile[2])) *
+                                                a.n_rot * d_in,
+                                     a.dx_bytes)
+                        : srcv[v].rlo;
       srcv[v].rw = make_rsrc(a.W + (size_t)c * 256 * d_in, (uint32_t)(256 * d_in * 2));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -527,7 +533,8 @@ struct PpArgs {
   const PfProItem* items;
   const DecVeraRow* vrows;      // [64 nvb]
   const uint16_t* A_sh;         // [r_v][d_in]
-  uint16_t* dx;                 // [n_rot][d_in] Delta rows by sorted position
+  uint16_t* dx;                 // [np][n_rot][d_in] Delta rows by sorted position (a rotation
+                                // item writes block pad / n_rot)
   float* tpart;                 // [shrink tiles][KP][4 waves][16][64] fp32 partial tiles
   uint16_t* tbf;                // [n][AW] finished sums in bf16
   int32_t* tcnt;                // [shrink tiles] arrival counters
@@ -580,7 +587,7 @@ __device__ void pp_rotate(const PpArgs& a, const PfProItem& it, int w, int m, in
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int row = 8 * (i >> 2) + 4 * h + (i & 3);
-      if (row < nr) a.dx[(size_t)(it.p0 + row) * d_in + col[cb]] = f2bf(acc[cb][i]);
+      if (row < nr) a.dx[(size_t)(it.pad + it.p0 + row) * d_in + col[cb]] = f2bf(acc[cb][i]);
     }
 }
 
@@ -595,7 +602,7 @@ __device__ void pp_rotate_scalar(const PpArgs& a, const PfProItem& it, int tid) 
     const uint16_t* xr = a.x + (size_t)ldg(a.perm + it.p0 + r) * d_in + kb * blk;
     float acc = 0.f;
     for (int i = 0; i < blk; ++i) acc += bf2f(ldg(xr + i)) * bf2f(ldg(prow + i));
-    a.dx[(size_t)(it.p0 + r) * d_in + col] = f2bf(acc);
+    a.dx[(size_t)(it.pad + it.p0 + r) * d_in + col] = f2bf(acc);
   }
 }
 
@@ -821,6 +828,9 @@ scute_status launch_prefill(scute_layer* L, const scute_batch* B, const void* x,
   ma.acc_bytes = P.tbf_bytes;
   ma.x_bytes = (uint32_t)((size_t)B->n * L->d_in * 2);
   ma.dx_bytes = (uint32_t)((size_t)B->n_rot * L->d_in * 2);
+  ma.n_rot = B->n_rot;
+  for (int32_t i = 0; i + 1 < MAX_PROJ; ++i)
+    ma.ptile[i] = (int32_t)((B->rproj && i + 1 < L->n_proj ? L->proj_end[i] : L->d_out) / 256);
   ma.d_in = (int32_t)L->d_in;
   ma.d_out = (int32_t)L->d_out;
   ma.RT = P.RT;

@@ -266,6 +266,19 @@ def run():
         fu.close()
         rows.append({"layer": "qkv", "tenants": name, "route": "fused", "us": t_fused})
         print(f"multiproj: {rows[-1]}", file=sys.stderr, flush=True)
+    # prefill: 2048 tokens with the OFT tenants (the fused layer takes the
+    # prefill path, its projections ending on 256-column tiles)
+    wls, tt = projection_workloads(qkv_tenants(True), 2048, d_in, d_outs, seed=12)
+    sp = QKVSplit(wls)
+    t_split = _time(torch, sp.forward, iters=50)
+    sp.close()
+    fu = QKVFused(wls, tt, len(qkv_tenants(True)))
+    t_fused = _time(torch, fu.forward, iters=50)
+    fu.close()
+    name = "lora+dora+ia3(k,v)+oft, 2048 tok"
+    rows += [{"layer": "qkv", "tenants": name, "route": "split", "us": t_split},
+             {"layer": "qkv", "tenants": name, "route": "fused", "us": t_fused}]
+    print(f"multiproj: {rows[-1]}", file=sys.stderr, flush=True)
     from synth import make_config
     up = make_config(3)  # FFN up 4096 -> 14336, 256 tokens, (IA)^3 + VeRA tenants
     Wg = np.random.default_rng(5).normal(0.0, 1.0 / np.sqrt(up.d_in), size=up.W.shape)

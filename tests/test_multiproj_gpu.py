@@ -109,16 +109,19 @@ def test_gated_up_projection_with_ia3():
 
 def test_qkv_fused_keeps_rotations_per_projection():
     """OFT tenants in the fused q / k / v layer: one rotation per projection.
-    100 rows run the two-launch decode path (each column tile stages its
-    projection's delta rows), 300 rows the generic kernels (one delta block
-    per projection); both against the per-projection oracles and the split
-    layers. The no-allocation forward refuses such a layer."""
+    100 rows run the two-launch decode path (each 64-column tile stages its
+    projection's delta rows); 300 rows run the prefill path when the
+    projections end on its 256-column tiles, else the generic kernels (one
+    delta block per projection). Each against the per-projection oracles and
+    the split layers. The no-allocation forward refuses such a layer."""
     _need_gpu()
     from lora_normal_form_amd import multiproj, scute
     ten = [(L, L, L), (O, O, O), (None, I3, I3), (O, None, L), (Dr, O, None)] * 2
-    for n, path in ((100, 1), (300, 0)):
-        wls, tt = multiproj.projection_workloads(ten, n, 512, (512, 128, 256), seed=95 + n, none_frac=0.1)
-        print(f"\n[gpu] qkv fused with OFT tenants, {n} rows", flush=True)
+    cases = [(100, (512, 128, 256), 1, "decode_main"), (300, (512, 128, 256), 0, "gemm"),
+             (300, (512, 256, 256), 2, "prefill_main")]
+    for n, d_outs, path, kernel in cases:
+        wls, tt = multiproj.projection_workloads(ten, n, 512, d_outs, seed=95 + n, none_frac=0.1)
+        print(f"\n[gpu] qkv fused with OFT tenants, {n} rows, {d_outs}", flush=True)
         fu = multiproj.QKVFused(wls, tt, len(ten))
         assert fu.batch.info()["path"] == path
         scute.scute_profile_enable(fu.layer.h, True)
@@ -126,7 +129,7 @@ def test_qkv_fused_keeps_rotations_per_projection():
         torch.cuda.synchronize()
         names = set(scute.scute_profile_read(fu.layer.h))
         scute.scute_profile_enable(fu.layer.h, False)
-        assert ("decode_main" in names) == (path == 1) and "fd_main" not in names, names
+        assert kernel in names and "fd_main" not in names, names
         sp = multiproj.QKVSplit(wls)
         ys = sp.forward()
         torch.cuda.synchronize()
