@@ -190,7 +190,8 @@ scute_status scute_layer_set_projections(scute_layer* layer, int32_t n_proj,
  * like the single rotation slot, the n_proj of them one after another
  * (scute_read_slot of SCUTE_SLOT_P returns n_proj d_in blk elements).
  * Batches with such rows run the two-launch decode path (bf16, up to 256
- * rows) or the generic kernels; scute_layer_forward_noalloc refuses them.
+ * rows), the prefill path (bf16, when every projection ends on a multiple
+ * of 256) or the generic kernels; scute_layer_forward_noalloc refuses them.
  * Errors: SCUTE_E_STATE if the layer has one projection or `id` is
  * occupied, SCUTE_E_INVALID for another method, a non-null desc->R or a
  * null R_proj, SCUTE_E_SHAPE for a bad block size; otherwise as
