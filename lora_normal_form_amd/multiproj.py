@@ -151,6 +151,8 @@ def fused_layer(wls, n_tenants, device=0):
                for (wl, ids), h in zip(wls, hosts)]
         fused.append(None if all(p is None for p in per) else fused_slots(per, d_outs))
     if any(f is not None and f["R_proj"] is not None for f in fused):
+        if any(d % 64 for d in d_outs[:-1]):
+            raise ValueError("rotations per projection need q and k widths that are multiples of 64")
         layer.set_projections(np.cumsum(d_outs))
     for t, f in enumerate(fused):
         if f is None:

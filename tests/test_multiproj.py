@@ -74,3 +74,7 @@ def test_fused_qkv_keeps_a_rotation_per_projection():
     wls, _ = multiproj.projection_workloads([(O, V, O)], 4, 32, d_outs, seed=5, dtype="f32", vera_rank=4)
     with pytest.raises(ValueError):
         multiproj.fused_layer(wls, 1, device=-1)
+    # projections must end on multiples of 64 when a tenant rotates
+    wls, _ = multiproj.projection_workloads([(O, O, O)], 4, 32, (48, 16, 64), seed=6, dtype="f32")
+    with pytest.raises(ValueError):
+        multiproj.fused_layer(wls, 1, device=-1)
