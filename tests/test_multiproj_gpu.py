@@ -144,3 +144,27 @@ def test_qkv_fused_keeps_rotations_per_projection():
             assert e.value.code == scute.E_UNSUPPORTED
         sp.close()
         fu.close()
+
+
+@pytest.mark.parametrize("n, path, kernel", [(128, 1, "decode_main"), (2048, 2, "prefill_main")])
+def test_qkv_fused_with_rotations_full_size(n, path, kernel):
+    """The q / k / v layer at its real shape, 4096 -> (4096, 1024, 1024), with
+    20 tenants of which four rotate (OFT, blocks of 32) on every projection:
+    128 decode tokens and 2048 prefill tokens, each projection against its
+    oracle."""
+    _need_gpu()
+    from lora_normal_form_amd import multiproj, scute
+    ten = multiproj.qkv_tenants(True)
+    wls, tt = multiproj.projection_workloads(ten, n, 4096, (4096, 1024, 1024), seed=12)
+    print(f"\n[gpu] qkv fused with OFT tenants, full size, {n} tokens", flush=True)
+    fu = multiproj.QKVFused(wls, tt, len(ten))
+    assert fu.batch.info()["path"] == path
+    scute.scute_profile_enable(fu.layer.h, True)
+    yf = fu.forward()
+    torch.cuda.synchronize()
+    names = set(scute.scute_profile_read(fu.layer.h))
+    scute.scute_profile_enable(fu.layer.h, False)
+    assert kernel in names, names
+    for (wl, _), a in zip(wls, yf):
+        _check(wl, a)
+    fu.close()
