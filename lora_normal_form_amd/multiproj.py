@@ -20,8 +20,11 @@ QKV, fused   one layer over W_qkv = [W_q; W_k; W_v] ([d_q + d_k + d_v][d_in]).
              it does not): the layer's projections are set to the q / k / v
              column ranges and the adapter loads with
              scute_load_adapter_proj, so OFT tenants keep the single GEMM.
-             Exact; not possible with a VeRA term (a different shared pair
-             per projection).
+             VeRA: each projection has its own shared pair, so the fused
+             layer's pair is theirs side by side, A_sh stacked and B_sh
+             block diagonal (its rank the sum of theirs), and a tenant's d
+             and e are its projections' concatenated (d zero on projections
+             without its VeRA term). Exact.
 QKV, split   three layers and three forwards; any method.
 FFN          a gate layer (base weight only) and the up layer with the
              tenants' adapters ((IA)^3's l on its s slot), then
@@ -94,16 +97,34 @@ class QKVSplit:
             ld.layer.close()
 
 
-def fused_slots(per_proj, d_outs):
+def fused_vera_pair(wls):
+    """The fused layer's shared VeRA pair from the projections' pairs: A_sh
+    [sum r][d_in] stacked, B_sh [sum d_out][sum r] block diagonal; with the
+    projections' ranks. None when no projection has a pair."""
+    ranks = [wl.vera_rank for wl, _ in wls]
+    if not any(ranks):
+        return None
+    d_in, d_outs = wls[0][0].d_in, [wl.d_out for wl, _ in wls]
+    A = np.zeros((sum(ranks), d_in))
+    B = np.zeros((sum(d_outs), sum(ranks)))
+    r0 = c0 = 0
+    for (wl, _), r, d in zip(wls, ranks, d_outs):
+        if r:
+            A[r0:r0 + r] = wl.A_sh
+            B[c0:c0 + d, r0:r0 + r] = wl.B_sh
+        r0, c0 = r0 + r, c0 + d
+    return A, B, ranks
+
+
+def fused_slots(per_proj, d_outs, vera_ranks=None):
     """One normal-form adapter's arrays from a tenant's per-projection folded
     slots (None for a projection it leaves alone). "R_proj" is None when no
-    projection rotates, else one rotation per projection (None: identity)."""
+    projection rotates, else one rotation per projection (None: identity).
+    vera_ranks: each projection's shared-pair rank (needed with a VeRA term)."""
     d_in = None
     for sl in per_proj:
         if sl is None:
             continue
-        if sl["vd"] is not None:
-            raise ValueError("a VeRA term needs the split q / k / v layers")
         if sl["A"] is not None:
             d_in = sl["A"].shape[1]
     rot = [sl is not None and sl["R_minus_I"] is not None for sl in per_proj]
@@ -118,7 +139,15 @@ def fused_slots(per_proj, d_outs):
     has_b = any(sl is not None and sl["b"] is not None for sl in per_proj)
     terms = [(p, sl["A"], sl["B"]) for p, sl in enumerate(per_proj) if sl is not None and sl["A"] is not None]
     out = {"s": s if has_s else None, "b": b if has_b else None, "rank": 0, "A": None, "B": None,
-           "R_proj": None, "blk": 0}
+           "R_proj": None, "blk": 0, "vd": None, "ve": None}
+    has_v = [sl is not None and sl["vd"] is not None for sl in per_proj]
+    if any(has_v):
+        if vera_ranks is None:
+            raise ValueError("a VeRA term needs the projections' shared-pair ranks")
+        out["vd"] = np.concatenate([sl["vd"] if v else np.zeros(r)
+                                    for sl, v, r in zip(per_proj, has_v, vera_ranks)])
+        out["ve"] = np.concatenate([sl["ve"] if v else np.ones(d)
+                                    for sl, v, d in zip(per_proj, has_v, d_outs)])
     if blks:
         blk = blks.pop()
         out["blk"] = blk
@@ -145,11 +174,21 @@ def fused_layer(wls, n_tenants, device=0):
     wl0 = wls[0][0]
     hosts = [glue.load(wl, device=-1, plan=False) for wl, _ in wls]
     layer = scute.Layer(wl0.d_in, sum(d_outs), wl0.dtype, max_adapters=max(1, n_tenants), device=device)
+    pair = fused_vera_pair(wls)
+    ranks = pair[2] if pair else None
     fused = []
     for t in range(n_tenants):
         per = [convert.slots(h.layer, ids[t], wl.d_in, wl.d_out, wl.vera_rank) if t in ids else None
                for (wl, ids), h in zip(wls, hosts)]
-        fused.append(None if all(p is None for p in per) else fused_slots(per, d_outs))
+        fused.append(None if all(p is None for p in per) else fused_slots(per, d_outs, ranks))
+    if pair is not None and any(f is not None and f["vd"] is not None for f in fused):
+        if device >= 0:
+            import torch
+            dev = torch.device("cuda", device)
+            A_f, B_f = glue.to_device(pair[0], wl0.dtype, dev), glue.to_device(pair[1], wl0.dtype, dev)
+        else:  # (a host-only layer keeps the pointers without reading them)
+            A_f, B_f = pair[0], pair[1]
+        layer.set_vera_shared(A_f, B_f, sum(ranks))
     if any(f is not None and f["R_proj"] is not None for f in fused):
         if any(d % 64 for d in d_outs[:-1]):
             raise ValueError("rotations per projection need q and k widths that are multiples of 64")
@@ -159,18 +198,19 @@ def fused_layer(wls, n_tenants, device=0):
             continue
         if f["R_proj"] is not None:
             layer.load_proj(t, f["R_proj"], f["blk"], rank=f["rank"], c=1.0, A=f["A"], B=f["B"], s=f["s"],
-                            b=f["b"])
+                            b=f["b"], vd=f["vd"], ve=f["ve"])
         else:
-            layer.load(t, "nf", rank=f["rank"], c=1.0, A=f["A"], B=f["B"], s=f["s"], b=f["b"])
+            layer.load(t, "nf", rank=f["rank"], c=1.0, A=f["A"], B=f["B"], s=f["s"], b=f["b"], vd=f["vd"],
+                       ve=f["ve"])
     for h in hosts:
         h.layer.close()
     return layer
 
 
 class QKVFused:
-    """q, k and v as one layer over the stacked weights (tenants without a
-    VeRA term; rotations per projection); forward returns the three column
-    slices."""
+    """q, k and v as one layer over the stacked weights (any method: rotations
+    per projection, the projections' VeRA pairs side by side); forward
+    returns the three column slices."""
 
     def __init__(self, wls, tenant_of_token, n_tenants, device=0, flags=0):
         import torch
@@ -241,13 +281,16 @@ def _time(torch, fn, iters=200, reps=7):
     return statistics.median(ts)
 
 
-def qkv_tenants(with_oft: bool):
+def qkv_tenants(with_oft: bool, with_vera: bool = False):
     from synth import AdapterSpec
     L, Dr, I3 = AdapterSpec("lora", rank=16), AdapterSpec("dora", rank=16), AdapterSpec("ia3")
     ten = [(L, L, L)] * 8 + [(Dr, Dr, Dr)] * 6 + [(None, I3, I3)] * 6
     if with_oft:
         O = AdapterSpec("oft", blk=32)
         ten = ten[:16] + [(O, O, O)] * 4
+    if with_vera:
+        V = AdapterSpec("vera")
+        ten = ten[:4] + [(V, V, V)] * 4 + ten[8:]
     return ten
 
 
@@ -255,13 +298,13 @@ def run():
     import torch
     rows = []
     d_in, d_outs, n = 4096, (4096, 1024, 1024), 128
-    for with_oft in (False, True):
-        ten = qkv_tenants(with_oft)
-        wls, tt = projection_workloads(ten, n, d_in, d_outs, seed=11)
+    for with_oft, with_vera in ((False, False), (True, False), (True, True)):
+        ten = qkv_tenants(with_oft, with_vera)
+        wls, tt = projection_workloads(ten, n, d_in, d_outs, seed=11, vera_rank=256 if with_vera else 0)
         sp = QKVSplit(wls)
         t_split = _time(torch, sp.forward)
         sp.close()
-        name = "lora+dora+ia3(k,v)" + ("+oft" if with_oft else "")
+        name = "lora+dora+ia3(k,v)" + ("+oft" if with_oft else "") + ("+vera" if with_vera else "")
         rows.append({"layer": "qkv", "tenants": name, "route": "split", "us": t_split})
         fu = QKVFused(wls, tt, len(ten))
         t_fused = _time(torch, fu.forward)

@@ -54,20 +54,30 @@ def test_qkv_fused_and_split_match_oracle():
     sp.close()
 
 
-def test_qkv_split_with_rotation_and_vera():
+@pytest.mark.parametrize("n, path", [(90, 1), (300, 2)])
+def test_qkv_split_and_fused_with_rotation_and_vera(n, path):
+    """OFT and VeRA tenants: the split layers, and the fused layer with a
+    rotation per projection and the projections' VeRA pairs side by side
+    (decode path at 90 rows, prefill path at 300), against the oracles."""
     _need_gpu()
     from lora_normal_form_amd import multiproj
-    ten = [(L, L, L), (O, O, O), (V, V, V), (None, I3, I3), (O, None, L)]
-    wls, _ = multiproj.projection_workloads(ten, 90, 512, (512, 128, 128), seed=92, vera_rank=64)
-    print("\n[gpu] qkv split with OFT and VeRA", flush=True)
+    ten = [(L, L, L), (O, O, O), (V, V, V), (None, I3, I3), (O, None, L), (V, None, Dr)]
+    wls, tt = multiproj.projection_workloads(ten, n, 512, (512, 256, 256), seed=92, vera_rank=64)
+    print(f"\n[gpu] qkv split with OFT and VeRA, {n} rows", flush=True)
     sp = multiproj.QKVSplit(wls)
     ys = sp.forward()
     torch.cuda.synchronize()
     for (wl, _), y in zip(wls, ys):
         _check(wl, y)
     sp.close()
-    with pytest.raises(ValueError):
-        multiproj.fused_layer(wls, len(ten), device=0)
+    print(f"[gpu] qkv fused with OFT and VeRA, {n} rows", flush=True)
+    fu = multiproj.QKVFused(wls, tt, len(ten))
+    assert fu.batch.info()["path"] == path
+    yf = fu.forward()
+    torch.cuda.synchronize()
+    for (wl, _), y in zip(wls, yf):
+        _check(wl, y)
+    fu.close()
 
 
 def test_gated_up_projection_with_ia3():
