@@ -178,3 +178,22 @@ def test_qkv_fused_with_rotations_full_size(n, path, kernel):
     for (wl, _), a in zip(wls, yf):
         _check(wl, a)
     fu.close()
+
+
+def test_qkv_fused_rotations_deterministic_plan():
+    """A deterministic plan of rows that rotate per projection: decode-size
+    batches run the generic kernels (no float atomics), so two forwards give
+    the same bits, and the output matches the oracles."""
+    _need_gpu()
+    from lora_normal_form_amd import multiproj, scute
+    ten = [(L, L, L), (O, O, O), (None, I3, I3), (O, None, L)]
+    wls, tt = multiproj.projection_workloads(ten, 64, 512, (512, 128, 256), seed=96)
+    fu = multiproj.QKVFused(wls, tt, len(ten), flags=scute.PLAN_DETERMINISTIC)
+    assert fu.batch.info()["path"] == 0
+    y1 = [t.clone() for t in fu.forward()]
+    y2 = fu.forward()
+    torch.cuda.synchronize()
+    for (wl, _), a, b in zip(wls, y1, y2):
+        assert torch.equal(a, b)
+        _check(wl, a)
+    fu.close()
