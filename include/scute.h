@@ -191,7 +191,7 @@ scute_status scute_layer_set_projections(scute_layer* layer, int32_t n_proj,
  * (scute_read_slot of SCUTE_SLOT_P returns n_proj d_in blk elements).
  * Batches with such rows run the two-launch decode path (bf16, up to 256
  * rows), the prefill path (bf16, when every projection ends on a multiple
- * of 256) or the generic kernels; scute_layer_forward_noalloc refuses them.
+ * of 256) or the generic kernels (so does scute_layer_forward_noalloc).
  * Errors: SCUTE_E_STATE if the layer has one projection or `id` is
  * occupied, SCUTE_E_INVALID for another method, a non-null desc->R or a
  * null R_proj, SCUTE_E_SHAPE for a bad block size; otherwise as
@@ -298,8 +298,9 @@ scute_status scute_layer_forward(scute_layer* layer, const scute_batch* batch,
  * scratch than there is; SCUTE_E_INVALID for null or misaligned pointers
  * (16-byte x, W, y; 4-byte token_adapter); SCUTE_E_STATE if a VeRA adapter
  * is loaded and the shared pair is not set; SCUTE_E_UNSUPPORTED on a
- * host-only layer, a device index past 63, or a layer holding an adapter
- * loaded with scute_load_adapter_proj. */
+ * host-only layer or a device index past 63. An adapter loaded with
+ * scute_load_adapter_proj makes the rotation output one block of n rows
+ * per projection (counted in the scratch a batch needs). */
 scute_status scute_layer_forward_noalloc(scute_layer* layer, const int32_t* token_adapter,
                                          int32_t n, const void* x, const void* W, float* y,
                                          void* stream);

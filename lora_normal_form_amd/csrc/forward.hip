@@ -532,11 +532,12 @@ void launch_noalloc(scute_layer* L, const int32_t* ta, int32_t n, const T* x, co
   const int64_t d_in = L->d_in, d_out = L->d_out;
   const int32_t na = L->max_adapters, rk = L->na_max_rank;
   const bool vera = L->n_vera_loaded > 0;
-  T* delta = (T*)ws;
+  T* delta = (T*)ws;  // one block of n rows per projection when an adapter rotates per projection
   float* t = (float*)(ws + o_t);
   float* u = (float*)(ws + o_u);
+  const unsigned npz = L->na_rproj ? (unsigned)L->n_proj : 1u;
   if (L->na_rot)
-    hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), n), dim3(256), 0, st, x, nullptr, ta,
+    hipLaunchKernelGGL(k_rotate_ref<T>, dim3(cdiv(d_in, 256), n, npz), dim3(256), 0, st, x, nullptr, ta,
                        L->table_dev, na, d_in, n, delta);
   if (rk > 0)
     hipLaunchKernelGGL(k_shrink_ref<T>, dim3(rk, n), dim3(256), 0, st, x, nullptr, ta, L->table_dev, na,
@@ -546,7 +547,7 @@ void launch_noalloc(scute_layer* L, const int32_t* ta, int32_t n, const T* x, co
                        L->table_dev, na, (const T*)L->A_sh, d_in, L->r_v, u);
   hipLaunchKernelGGL(k_gemm_ref<T>, dim3(cdiv(d_out, 32), cdiv(n, 32)), dim3(256), 0, st, x, W,
                      (const T*)delta, nullptr, ta, L->table_dev, na, n, L->na_rot ? n : 0, d_in, d_out,
-                     proj_starts(L, false), y);
+                     proj_starts(L, L->na_rproj), y);
   if (rk > 0 || vera)
     hipLaunchKernelGGL(k_expand_ref<T>, dim3(cdiv(d_out, 256), n), dim3(256), 0, st, t, u,
                        (const T*)L->B_sh, nullptr, ta, L->table_dev, na, rk, L->r_v, d_out, y);
@@ -587,12 +588,10 @@ extern "C" scute_status scute_layer_forward_noalloc(scute_layer* L, const int32_
     if (vera && (!L->A_sh || !L->B_sh))
       return fail(SCUTE_E_STATE, "scute_layer_forward_noalloc: shared VeRA pair not set");
     layer_facts(L);
-    if (L->na_rproj)
-      return fail(SCUTE_E_UNSUPPORTED,
-                  "scute_layer_forward_noalloc: an adapter rotates per projection (use scute_layer_forward)");
     auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
     const size_t es = dtype_size(L->act);
-    const size_t o_t = L->na_rot ? al((size_t)n * L->d_in * es) : 0;
+    const size_t npz = L->na_rproj ? (size_t)L->n_proj : 1;  // delta blocks
+    const size_t o_t = L->na_rot ? al(npz * n * L->d_in * es) : 0;
     const size_t o_u = o_t + al((size_t)n * L->na_max_rank * 4);
     const size_t need = o_u + (vera ? (size_t)n * L->r_v * 4 : 0);
     if (need > (size_t)SCUTE_NOALLOC_SCRATCH_BYTES)
