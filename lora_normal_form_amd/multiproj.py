@@ -228,7 +228,7 @@ class QKVFused:
     def forward(self):
         self.layer.forward(self.batch, self.x, self.W, self.y)
         offs = np.concatenate([[0], np.cumsum(self.d_outs)])
-        return [self.y[:, offs[p]:offs[p + 1]] for p in range(3)]
+        return [self.y[:, offs[p]:offs[p + 1]] for p in range(len(self.d_outs))]
 
     def close(self):
         self.batch.close()

@@ -202,3 +202,21 @@ def test_qkv_fused_rotations_deterministic_plan():
         assert torch.equal(a, b)
         _check(wl, a)
     fu.close()
+
+
+def test_four_projections_with_rotations():
+    """Four projections (the most a layer takes), each tenant rotating some
+    of them: decode path, against each projection's oracle."""
+    _need_gpu()
+    from lora_normal_form_amd import multiproj
+    ten = [(O, O, None, O), (L, O, O, None), (I3, None, L, O), (Dr, Dr, Dr, Dr)]
+    d_outs = (256, 128, 64, 192)
+    wls, tt = multiproj.projection_workloads(ten, 80, 512, d_outs, seed=97, none_frac=0.1)
+    fu = multiproj.QKVFused(wls, tt, len(ten))
+    assert fu.layer.h and fu.batch.info()["path"] == 1
+    ys = fu.forward()
+    torch.cuda.synchronize()
+    assert len(ys) == 4
+    for (wl, _), y in zip(wls, ys):
+        _check(wl, y)
+    fu.close()
