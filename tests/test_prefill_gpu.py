@@ -7,6 +7,7 @@ Bars as in test_parity_gpu: max|y - ref| <= 1e-2 max|ref| and every touched
 adapter's mean effect error <= 1% of its effect.
 """
 
+import dataclasses
 import os
 
 import numpy as np
@@ -241,3 +242,21 @@ def test_prefill_ranks_not_multiple_of_8():
     ld = _load(wl)
     assert ld.batch.info()["path"] == PREFILL, ld.batch.info()
     _check(wl, _forward(ld))
+
+
+def test_prefill_long_batch_sampled_rows():
+    # 16384 tokens at 4096 -> 4096 (eight times the prefill workload's
+    # batch): every method in ragged segments, tokens in random order. The
+    # oracle checks 1024 rows sampled across the batch (each row's output
+    # depends only on its own x and adapter).
+    _need_gpu()
+    rng = np.random.default_rng(41)
+    ta = rng.integers(-1, len(MIX), size=16384)
+    wl = _wl("prefill_long", ta, seed=41, d_out=4096)
+    ld = _load(wl)
+    assert ld.batch.info()["path"] == PREFILL
+    y = _forward(ld)
+    idx = np.sort(rng.choice(wl.n, size=1024, replace=False))
+    sub = dataclasses.replace(wl, name="prefill_long_sample", n=len(idx), x=wl.x[idx],
+                              token_adapter=wl.token_adapter[idx])
+    _check(sub, y[idx])
