@@ -548,6 +548,8 @@ scute_status store_adapter(scute_layer* L, int32_t id, const FoldOut& F, int32_t
   return SCUTE_OK;
 }
 
+// Arguments every load checks: a layer and a descriptor, an id in range
+// and not occupied.
 scute_status load_checks(const scute_layer* L, int32_t id, const void* D, const char* fn) {
   if (!L || !D) return fail(SCUTE_E_INVALID, std::string(fn) + ": null argument");
   if (id < 0 || id >= L->max_adapters) return fail(SCUTE_E_INVALID, std::string(fn) + ": id out of range");
@@ -573,6 +575,11 @@ extern "C" scute_status scute_load_adapter(scute_layer* L, int32_t id, const scu
   }
 }
 
+// A normal-form adapter with one rotation per projection of the layer: the
+// descriptor's other slots fold as for scute_load_adapter, and the P slot
+// holds n_proj rotations, (R_p - I)^T per block, one after another (a null
+// R_p is the identity, stored as zeros). "How does Scute plug into vLLM?"
+// (explainer): OFT gives the q, k and v projections their own rotations.
 extern "C" scute_status scute_load_adapter_proj(scute_layer* L, int32_t id, const scute_adapter_desc* D,
                                                 const void* const* R_proj, const void* W_host,
                                                 void* stream) {
@@ -605,6 +612,9 @@ extern "C" scute_status scute_load_adapter_proj(scute_layer* L, int32_t id, cons
   }
 }
 
+// Output column ranges that may take their own rotation (ends checked:
+// increasing, all but the last on 64-column tiles, the last d_out); only
+// while no adapter is loaded, so no stored rotation disagrees with them.
 extern "C" scute_status scute_layer_set_projections(scute_layer* L, int32_t n_proj, const int64_t* col_end) {
   if (!L || !col_end) return fail(SCUTE_E_INVALID, "scute_layer_set_projections: null argument");
   if (n_proj < 1 || n_proj > MAX_PROJ)
