@@ -220,3 +220,48 @@ def test_four_projections_with_rotations():
     for (wl, _), y in zip(wls, ys):
         _check(wl, y)
     fu.close()
+
+
+@pytest.mark.parametrize("n, path", [(96, 1), (320, 0)])
+def test_single_and_per_projection_rotations_together(n, path):
+    """A layer with projections holding an adapter with one rotation per
+    projection (scute_load_adapter_proj) and one with a single rotation for
+    every column (scute_load_adapter, normal form with R): the single
+    rotation serves each projection's delta block. Decode path at 96 rows,
+    generic kernels at 320 (the projections do not end on 256-column tiles);
+    each projection against the oracle."""
+    _need_gpu()
+    from synth import Adapter, Workload, round_bf16
+    from lora_normal_form_amd import scute
+    from lora_normal_form_amd import workload as glue
+    rng = np.random.default_rng(98 + n)
+    d_in, d_outs, blk = 512, (256, 128, 128), 32
+
+    def rotation():
+        q = rng.normal(0.0, 0.05, size=(d_in // blk, blk, blk))
+        return np.stack([oracle.cayley(qq - qq.T) for qq in q])
+
+    R_proj, R_one = [rotation() for _ in d_outs], rotation()
+    x = round_bf16(rng.normal(0.0, 1.0, size=(n, d_in)))
+    Ws = [round_bf16(rng.normal(0.0, 1.0 / np.sqrt(d_in), size=(d, d_in))) for d in d_outs]
+    ta = rng.integers(-1, 2, size=n)
+    L_ = scute.Layer(d_in, sum(d_outs), "bf16", max_adapters=2, device=0)
+    L_.set_projections(np.cumsum(d_outs))
+    L_.load_proj(0, R_proj, blk)
+    L_.load(1, "nf", blk=blk, R=R_one)
+    batch = L_.plan(ta)
+    assert batch.info()["path"] == path
+    dev = torch.device("cuda", 0)
+    xd = glue.to_device(x, "bf16", dev)
+    Wd = glue.to_device(np.concatenate(Ws, 0), "bf16", dev)
+    y = torch.full((n, sum(d_outs)), float("nan"), dtype=torch.float32, device=dev)
+    L_.forward(batch, xd, Wd, y)
+    torch.cuda.synchronize()
+    offs = np.concatenate([[0], np.cumsum(d_outs)])
+    for p, (d, Wp) in enumerate(zip(d_outs, Ws)):
+        wl = Workload(f"rot_mix_p{p}", "bf16", d_in, d, n, x, Wp,
+                      [Adapter(0, "nf", blk=blk, R=R_proj[p]), Adapter(1, "nf", blk=blk, R=R_one)],
+                      np.asarray(ta, dtype=np.int64))
+        _check(wl, y[:, offs[p]:offs[p + 1]])
+    batch.close()
+    L_.close()
