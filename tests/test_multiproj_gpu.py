@@ -222,20 +222,21 @@ def test_four_projections_with_rotations():
     fu.close()
 
 
-@pytest.mark.parametrize("n, path", [(96, 1), (320, 0)])
-def test_single_and_per_projection_rotations_together(n, path):
+@pytest.mark.parametrize("n, d_outs, path", [(96, (256, 128, 128), 1), (320, (256, 128, 128), 0),
+                                            (320, (256, 256, 256), 2)])
+def test_single_and_per_projection_rotations_together(n, d_outs, path):
     """A layer with projections holding an adapter with one rotation per
     projection (scute_load_adapter_proj) and one with a single rotation for
     every column (scute_load_adapter, normal form with R): the single
-    rotation serves each projection's delta block. Decode path at 96 rows,
-    generic kernels at 320 (the projections do not end on 256-column tiles);
-    each projection against the oracle."""
+    rotation serves each projection's delta block. Decode path at 96 rows;
+    at 320 the prefill path when the projections end on 256-column tiles,
+    else the generic kernels; each projection against the oracle."""
     _need_gpu()
     from synth import Adapter, Workload, round_bf16
     from lora_normal_form_amd import scute
     from lora_normal_form_amd import workload as glue
-    rng = np.random.default_rng(98 + n)
-    d_in, d_outs, blk = 512, (256, 128, 128), 32
+    rng = np.random.default_rng(98 + n + len(set(d_outs)))
+    d_in, blk = 512, 32
 
     def rotation():
         q = rng.normal(0.0, 0.05, size=(d_in // blk, blk, blk))
