@@ -364,6 +364,17 @@ typedef struct scute_batch_info {
 
 scute_status scute_batch_info_get(const scute_batch* batch, scute_batch_info* out);
 
+/* Whether a forward of this plan had a cross-work-group wait give up
+ * (*out = 1) since the plan was built or last reset (*out = 0 otherwise).
+ * Only the fused decode path waits across work-groups; its waits are bounded
+ * (about 2^20 polls) and a wait that gives up records the failure and lets
+ * the kernel finish instead of hanging, so that forward's output is not
+ * valid. Call after synchronising the stream the forwards ran on; the read
+ * is a blocking device-to-host copy. reset != 0 clears the flag afterwards.
+ * Errors: SCUTE_E_INVALID for null pointers, SCUTE_E_HIP if the copy fails.
+ * Plans on other paths always report 0. */
+scute_status scute_batch_wait_failures(const scute_batch* batch, int32_t reset, int32_t* out);
+
 /* Copy the plan's tables to HOST memory:
  *   perm[n]            token index at each sorted position
  *   seg[3*n_segments]  (adapter id, first sorted position, length) per run

@@ -111,6 +111,8 @@ struct FdArgs {
   int32_t* err;
   int32_t d_in, d_out, MG, g_rot, S, C, RT, AW, k_chunk, gv0, gv1;
   int32_t CG;  // column tiles of the grid (tiles past d_out carry shrink blocks only)
+  int32_t spin_limit;  // polls before a wait gives up
+  uint32_t wait_bias;  // added to the forward number the waits look for (0; 1 makes them fail)
 };
 
 // W and the wave's shrink-block rows of one stage. W: the wave's 32 W rows
@@ -286,15 +288,15 @@ __device__ __forceinline__ void fd_load_bv(const FdArgs& a, int s0, int nks, int
     if (s0 + j < nks) bv[j] = ldb16(bsr, (uint32_t)((fm * a.r_v + 16 * (s0 + j) + 8 * h) * 2));
 }
 
-// Bounded wait (~2^20 polls) until `ready` holds in every lane; a wait that
-// gives up records the failure in the error flag and goes on.
+// Bounded wait (spin_limit polls, ~2^20) until `ready` holds in every lane;
+// a wait that gives up records the failure in the error flag and goes on.
 template <typename F>
 __device__ __forceinline__ void fd_wait(const FdArgs& a, int lane, F ready) {
   int spins = 0;
   for (;;) {
     if (__ballot(!ready()) == 0) return;
     __builtin_amdgcn_s_sleep(2);
-    if (++spins > (1 << 20)) {
+    if (++spins > a.spin_limit) {
       if (lane == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       return;
     }
@@ -335,7 +337,7 @@ __device__ void fd_finish_piece(const FdArgs& a, const FdRow& rr, const f32x16& 
   issue_fence();
   // (b) every slice's piece stored: its arrival count grows by S per forward
   if (a.S > 1) {
-    const uint32_t need = (uint32_t)a.S * a.epoch;
+    const uint32_t need = (uint32_t)a.S * (a.epoch + a.wait_bias);
     fd_wait(a, lane, [&] {
       return lane != 0 ||
              (int)((uint32_t)__hip_atomic_load(pcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) - need) >= 0;
@@ -376,7 +378,8 @@ __device__ void fd_finish_piece(const FdArgs& a, const FdRow& rr, const f32x16& 
     for (int j0 = 0; j0 < nb; j0 += 64)
       fd_wait(a, lane, [&] {
         return j0 + lane >= nb ||
-               __hip_atomic_load(a.xdone + b0 + j0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == a.epoch;
+               __hip_atomic_load(a.xdone + b0 + j0 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+                   a.epoch + a.wait_bias;
       });
   }
   const rsrc_t racc = make_rsrc(a.acc, a.acc_bytes);
@@ -715,6 +718,8 @@ scute_status launch_fdecode(scute_layer* L, const scute_batch* B, const void* x,
   a.gv0 = P.gv0;
   a.gv1 = P.gv1;
   a.CG = P.CG;
+  a.spin_limit = P.spin_limit;
+  a.wait_bias = P.wait_bias;
   if (!a.rows || !a.goff || !a.xoff || !a.acc || !a.cnt || !a.err ||
       (P.n_xb > 0 && (!a.xb || !a.xpart || !a.xcnt || !a.xdone)) ||
       (P.S > 1 && !a.part) || (B->n_rot > 0 && !a.dx) || (P.gv1 > P.gv0 && !a.B_sh))

@@ -265,7 +265,9 @@ struct FdPlan {
   uint32_t* xdone = nullptr;       // [n_xb] forward number whose sums the block holds
   float* part = nullptr;           // [C][S][MG][4][4 KB] split-K partial pieces
   int32_t* cnt = nullptr;          // [C][MG][4] arrival counters (never reset)
-  int32_t* err = nullptr;          // bounded waits that gave up
+  int32_t* err = nullptr;          // bounded waits that gave up (scute_batch_wait_failures)
+  int32_t spin_limit = 1 << 20;    // polls before a wait gives up
+  uint32_t wait_bias = 0;          // 1: the waits look for a forward that never comes (tests)
   uint32_t acc_bytes = 0, part_bytes = 0, xpart_bytes = 0;
   mutable uint32_t fwd = 0;        // forwards launched with this plan
 };

@@ -216,6 +216,27 @@ extern "C" scute_status scute_batch_info_get(const scute_batch* B, scute_batch_i
   return SCUTE_OK;
 }
 
+// The fused decode path's error flag: its cross-work-group waits are
+// bounded, and a wait that gives up sets the flag instead of hanging.
+extern "C" scute_status scute_batch_wait_failures(const scute_batch* B, int32_t reset, int32_t* out) {
+  if (!B || !out) return fail(SCUTE_E_INVALID, "scute_batch_wait_failures: null argument");
+  *out = 0;
+  if (!B->fp.enabled || !B->fp.err) return SCUTE_OK;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  if (prev != B->device) (void)hipSetDevice(B->device);
+  int32_t v = 0;
+  hipError_t e = hipMemcpy(&v, B->fp.err, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) {
+    const int32_t zero = 0;
+    e = hipMemcpy(B->fp.err, &zero, 4, hipMemcpyHostToDevice);
+  }
+  if (prev != B->device && prev >= 0) (void)hipSetDevice(prev);
+  if (e != hipSuccess) return hip_fail(e, "scute_batch_wait_failures");
+  *out = v != 0;
+  return SCUTE_OK;
+}
+
 extern "C" scute_status scute_batch_read(const scute_batch* B, int32_t* perm, int32_t* seg) {
   if (!B) return fail(SCUTE_E_INVALID, "scute_batch_read: batch is null");
   if (perm && B->n) memcpy(perm, B->perm.data(), 4 * (size_t)B->n);

@@ -322,6 +322,14 @@ scute_status build_fdecode_plan(const scute_layer* L, scute_batch* B, hipStream_
   F.acc_bytes = (uint32_t)acc_bytes;
   F.part_bytes = (uint32_t)part_bytes;
   F.fwd = 0;
+  // SCUTE_FD_FORCE_WAIT_FAIL=1 (tests of the failure report): every wait
+  // looks for a forward number no arrival reaches and gives up after a few
+  // polls, so each wave still finishes; the output of such a forward is not
+  // valid and scute_batch_wait_failures reports it
+  if (env_int("SCUTE_FD_FORCE_WAIT_FAIL", 0) == 1) {
+    F.spin_limit = 16;
+    F.wait_bias = 1;
+  }
   F.enabled = true;
   return SCUTE_OK;
 }

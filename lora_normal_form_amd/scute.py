@@ -91,6 +91,7 @@ SIGNATURES = {
     "scute_read_slot": (C.c_int32, [_P, C.c_int32, C.c_int32, _P, C.c_int64]),
     "scute_batch_info_get": (C.c_int32, [_P, C.POINTER(BatchInfo)]),
     "scute_batch_read": (C.c_int32, [_P, _P, _P]),
+    "scute_batch_wait_failures": (C.c_int32, [_P, C.c_int32, C.POINTER(C.c_int32)]),
     "scute_profile_enable": (C.c_int32, [_P, C.c_int32]),
     "scute_profile_read": (C.c_int32, [_P, C.POINTER(KernelTime), C.c_int32,
                                        C.POINTER(C.c_int32)]),
@@ -288,6 +289,12 @@ def scute_profile_read(layer: int) -> Dict[str, Dict]:
             for i in range(min(cnt.value, cap))}
 
 
+def scute_batch_wait_failures(batch: int, reset: bool = False) -> int:
+    out = C.c_int32(0)
+    _check(lib.scute_batch_wait_failures(batch, 1 if reset else 0, C.byref(out)))
+    return out.value
+
+
 def scute_last_error() -> str:
     return lib.scute_last_error().decode()
 
@@ -428,3 +435,8 @@ class Batch:
 
     def read(self):
         return scute_batch_read(self.h)
+
+    def wait_failures(self, reset=False):
+        """1 if a forward of this plan had a bounded wait give up (fused decode
+        path), else 0; reset clears it."""
+        return scute_batch_wait_failures(self.h, reset)

@@ -339,3 +339,24 @@ def test_decode_overflow_rows_take_the_prefill_path():
                                     assign="explicit", token_adapter=ta, seed=72))
     _, y = _forward(wl, expect_path=2)
     _check(wl, y)
+
+
+def test_fused_wait_failures_are_reported(decode_mode):
+    # the fused path's cross-work-group waits are bounded: a plan whose waits
+    # the host makes fail (SCUTE_FD_FORCE_WAIT_FAIL: they look for a forward
+    # no arrival reaches and give up after a few polls) reports the failure
+    # after its forward, and every wave still finishes; a normal plan of the
+    # same batch reports none and matches the oracle
+    _need_gpu()
+    if decode_mode != 1:
+        pytest.skip("only the fused path waits across work-groups")
+    wl = make_workload(WorkloadSpec("waits", "bf16", 1024, 1024, 96,
+                                    [AdapterSpec("lora", rank=16), AdapterSpec("vera"), AdapterSpec("ia3")],
+                                    vera_rank=64, seed=61))
+    ld, y = _forward(wl, expect_path=1)
+    assert ld.batch.wait_failures() == 0
+    _check(wl, y)
+    bad, _ = _forward(wl, expect_path=1, SCUTE_FD_FORCE_WAIT_FAIL=1)
+    assert bad.batch.wait_failures() == 1
+    assert bad.batch.wait_failures(reset=True) == 1
+    assert bad.batch.wait_failures() == 0

@@ -256,6 +256,8 @@ def test_error_paths_leave_layer_usable():
     assert _err(L.forward, b, 16, 16, 16) == scute.E_STATE
     b2 = L.plan([1, 0])
     assert _err(L.forward, b2, 16, 16, 16) == scute.E_UNSUPPORTED              # host-only
+    assert b2.wait_failures() == 0                                             # no fused path
+    assert _err(scute.scute_batch_wait_failures, 0) == scute.E_INVALID
     L2 = scute.Layer(32, 16, "f32", max_adapters=4, device=-1)
     assert _err(scute.scute_cost_model, L2.h, b2.h) == scute.E_STATE           # other layer
     assert _err(L.unload, 3) == scute.E_STATE
